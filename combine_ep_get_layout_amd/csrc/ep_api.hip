@@ -1,0 +1,263 @@
+// C ABI of libep: argument validation, workspace carve-up and launches.
+// Declarations, semantics and the passages each call follows: include/ep.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ep.h"
+#include "ep_internal.hpp"
+
+namespace ep {
+size_t message_ws_bytes(int R);
+}
+
+using ep::Geometry;
+
+namespace {
+
+constexpr int kBatches = 16;  // batches of entries per layout chunk
+
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline int bits_for(int n) {  // bits to represent 0..n-1
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+int ep::make_geometry(const ep_problem* p, Geometry* g) {
+  if (!p) return EP_ERR_NULL;
+  const int R = p->num_ranks, T = p->num_tokens, H = p->hidden, E = p->num_experts,
+            K = p->num_topk;
+  if (p->reserved != 0) return EP_ERR_SHAPE;
+  if (p->mode < EP_MODE_NORMAL || p->mode > EP_MODE_MESSAGES) return EP_ERR_MODE;
+  if (p->quant < EP_QUANT_NONE || p->quant > EP_QUANT_FP8_UE8M0) return EP_ERR_MODE;
+  if (R < 1 || R > 256 || T < 0 || K < 1 || K > 64) return EP_ERR_SHAPE;
+  if (E < R || E > 2048 || E % R != 0) return EP_ERR_SHAPE;
+  if (H < 8 || H % 8 != 0 || H > (1 << 20)) return EP_ERR_SHAPE;
+  if (p->quant != EP_QUANT_NONE && H % 128 != 0) return EP_ERR_SHAPE;
+  if (p->expert_alignment < 1) return EP_ERR_SHAPE;
+  const int64_t entries = (int64_t)R * T * K;
+  if (entries >= (1ll << 31) || (int64_t)R * T * R >= (1ll << 31)) return EP_ERR_SHAPE;
+  if (p->mode == EP_MODE_LOW_LATENCY) {
+    if ((int64_t)E * R * T >= (1ll << 31)) return EP_ERR_SHAPE;
+  } else {
+    // worst-case aligned rows must stay below 2^31
+    if (entries + (int64_t)E * (p->expert_alignment - 1) >= (1ll << 31)) return EP_ERR_SHAPE;
+  }
+  if (p->mode == EP_MODE_MESSAGES) {
+    if (p->region_bytes < 16 || p->region_bytes % 16 != 0) return EP_ERR_SHAPE;
+  }
+  g->R = R;
+  g->T = T;
+  g->H = H;
+  g->E = E;
+  g->K = K;
+  g->L = E / R;
+  g->G = H / 128;
+  int tb = 64 / K;
+  const int cap = 2048 / R;  // LDS row buffer of tb*R ints
+  if (tb > cap) tb = cap;
+  if (tb < 1) tb = 1;
+  g->tb = tb;
+  g->ct = tb * kBatches;
+  g->C = (T + g->ct - 1) / g->ct;
+  g->NC = R * g->C;
+  g->ebits = bits_for(E);
+  g->rbits = bits_for(R);
+  size_t off = 0;
+  g->off_hist_e = off;
+  off += up256(sizeof(int32_t) * (size_t)E * g->NC);
+  g->off_hist_r = off;
+  off += up256(sizeof(int32_t) * (size_t)R * g->NC);
+  g->off_local_e = off;
+  off += up256(sizeof(int32_t) * (size_t)entries);
+  g->off_local_r = off;
+  off += up256(sizeof(int32_t) * (size_t)R * T * R);
+  g->off_msg = off;
+  if (p->mode == EP_MODE_MESSAGES) off += up256(message_ws_bytes(R));
+  g->ws_bytes = off < 256 ? 256 : off;
+  return EP_OK;
+}
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_problem* p) {
+  Geometry g;
+  if (ep::make_geometry(p, &g) != EP_OK) return 0;
+  return g.ws_bytes;
+}
+
+int64_t ep_max_recv_rows(const ep_problem* p) {
+  Geometry g;
+  if (ep::make_geometry(p, &g) != EP_OK) return -1;
+  if (p->mode == EP_MODE_LOW_LATENCY) return (int64_t)g.E * g.R * g.T;
+  return (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+}
+
+const char* ep_status_string(int s) {
+  switch (s) {
+    case EP_OK: return "ok";
+    case EP_ERR_NULL: return "a required pointer is NULL";
+    case EP_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case EP_ERR_SHAPE: return "inconsistent or out-of-limit sizes";
+    case EP_ERR_MODE: return "unknown or unsupported mode / quantisation";
+    case EP_ERR_WORKSPACE: return "workspace too small";
+    case EP_ERR_CAPACITY: return "capacity too small";
+    case EP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  // arrays with one entry per token may be NULL when there are no tokens
+  const bool toks = (int64_t)g.R * g.T > 0;
+  if (!out || !out->num_tokens_per_rank || !out->num_tokens_per_expert ||
+      !out->rank_prefix_matrix || !out->recv_tokens_per_expert || !out->expert_start ||
+      !out->rows_per_rank || !out->row_base || !out->err || !workspace)
+    return EP_ERR_NULL;
+  if (toks && (!topk_idx || !out->is_token_in_rank)) return EP_ERR_NULL;
+  if (toks && p->mode != EP_MODE_MESSAGES && !out->send_pos) return EP_ERR_NULL;
+  if (toks && p->mode == EP_MODE_MESSAGES && !out->send_head) return EP_ERR_NULL;
+  const void* ints[] = {topk_idx, out->num_tokens_per_rank, out->num_tokens_per_expert,
+                        out->rank_prefix_matrix, out->recv_tokens_per_expert, out->expert_start,
+                        out->rows_per_rank, out->row_base, out->send_pos, out->send_head,
+                        out->recv_src_idx, out->err};
+  for (const void* q : ints)
+    if (q && !aligned(q, 4)) return EP_ERR_ALIGN;
+  if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
+  if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
+  if (out->recv_src_idx && out->recv_capacity < 0) return EP_ERR_CAPACITY;
+
+  ep::LayoutArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = g;
+  a.mode = p->mode;
+  a.align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;
+  a.topk = topk_idx;
+  a.cnt_rank = out->num_tokens_per_rank;
+  a.cnt_expert = out->num_tokens_per_expert;
+  a.in_rank = out->is_token_in_rank;
+  a.rpm = out->rank_prefix_matrix;
+  a.recv_per_expert = out->recv_tokens_per_expert;
+  a.expert_start = out->expert_start;
+  a.rows = out->rows_per_rank;
+  a.row_base = out->row_base;
+  a.send_pos = out->send_pos;
+  a.send_head = out->send_head;
+  a.recv_src_idx = out->recv_src_idx;
+  a.recv_cap = out->recv_capacity;
+  a.err = out->err;
+  char* ws = (char*)workspace;
+  a.hist_e = (int32_t*)(ws + g.off_hist_e);
+  a.hist_r = (int32_t*)(ws + g.off_hist_r);
+  a.local_e = (int32_t*)(ws + g.off_local_e);
+  a.local_r = (int32_t*)(ws + g.off_local_r);
+  if (ep::launch_layout(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
+int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
+                const int32_t* topk_idx, const float* topk_weights, const ep_recv* recv,
+                const ep_messages* msgs, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  const bool toks = (int64_t)g.R * g.T > 0;
+  if (!layout || !layout->err || (toks && !x)) return EP_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(layout->err, 4)) return EP_ERR_ALIGN;
+  if (p->mode != EP_MODE_MESSAGES) {
+    if (!recv) return EP_ERR_NULL;
+    if (toks && (!recv->x || !layout->send_pos)) return EP_ERR_NULL;
+    if (toks && p->quant != EP_QUANT_NONE && !recv->scales) return EP_ERR_NULL;
+    if (!aligned(recv->x, 16) || !aligned(layout->send_pos, 4)) return EP_ERR_ALIGN;
+    if (recv->scales && !aligned(recv->scales, 4)) return EP_ERR_ALIGN;
+    if (recv->capacity < 0) return EP_ERR_CAPACITY;
+    if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
+      return EP_ERR_CAPACITY;
+    ep::DispatchArgs a;
+    a.g = g;
+    a.mode = p->mode;
+    a.quant = p->quant;
+    a.x = x;
+    a.send_pos = layout->send_pos;
+    a.recv_x = recv->x;
+    a.recv_scales = recv->scales;
+    a.cap = recv->capacity;
+    // low-latency rows never leave the E blocks of R*T rows the scales cover
+    if (p->mode == EP_MODE_LOW_LATENCY) a.cap = (int64_t)g.E * g.R * g.T;
+    a.err = layout->err;
+    if (ep::launch_dispatch(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+    return EP_OK;
+  }
+  // message mode
+  if (!msgs || !topk_idx || !topk_weights || !layout->send_head || !layout->num_tokens_per_rank ||
+      !msgs->send_arena || !msgs->table || !msgs->arena_base || !msgs->descriptors ||
+      !msgs->num_descriptors || !workspace)
+    return EP_ERR_NULL;
+  if (!aligned(msgs->send_arena, 16) || !aligned(msgs->descriptors, 16) ||
+      !aligned(msgs->table, 8) || !aligned(msgs->arena_base, 8) ||
+      !aligned(msgs->num_descriptors, 8) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+      !aligned(layout->send_head, 4) || !aligned(layout->num_tokens_per_rank, 4) ||
+      !aligned(workspace, 16))
+    return EP_ERR_ALIGN;
+  if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
+  if (msgs->send_capacity < 0 || msgs->desc_capacity < 0) return EP_ERR_CAPACITY;
+  ep::MessageArgs a;
+  a.g = g;
+  a.quant = p->quant;
+  a.region_bytes = p->region_bytes;
+  a.epoch = p->epoch;
+  a.x = x;
+  a.topk = topk_idx;
+  a.w = topk_weights;
+  a.cnt_rank = layout->num_tokens_per_rank;
+  a.send_head = layout->send_head;
+  a.arena = msgs->send_arena;
+  a.arena_cap = msgs->send_capacity;
+  a.table = msgs->table;
+  a.arena_base = msgs->arena_base;
+  a.desc = msgs->descriptors;
+  a.desc_cap = msgs->desc_capacity;
+  a.num_desc = msgs->num_descriptors;
+  a.err = layout->err;
+  a.ws = (char*)workspace + g.off_msg;
+  if (ep::launch_messages(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
+int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y, int64_t y_rows,
+               const float* topk_weights, uint16_t* out, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (p->mode == EP_MODE_MESSAGES) return EP_ERR_MODE;
+  const bool toks = (int64_t)g.R * g.T > 0;
+  if (!layout || !layout->err) return EP_ERR_NULL;
+  if (toks && (!layout->send_pos || !topk_weights || !out || (!y && y_rows > 0)))
+    return EP_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) ||
+      !aligned(layout->send_pos, 4) || !aligned(layout->err, 4))
+    return EP_ERR_ALIGN;
+  if (y_rows < 0) return EP_ERR_CAPACITY;
+  ep::CombineArgs a;
+  a.g = g;
+  a.y = y;
+  a.y_rows = y_rows;
+  a.send_pos = layout->send_pos;
+  a.w = topk_weights;
+  a.out = out;
+  a.err = layout->err;
+  if (ep::launch_combine(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Host/device shared declarations internal to libep (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ep.h"
+
+namespace ep {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Token chunking used by the layout kernels: one wavefront walks a chunk of
+// consecutive tokens of one source rank in batches of `tb` tokens (tb*K
+// entries <= 64, one entry per lane).
+struct Geometry {
+  int R, T, H, E, K, L, G;
+  int tb;      // tokens per batch
+  int ct;      // tokens per chunk
+  int C;       // chunks per source rank
+  int NC;      // R * C
+  int ebits;   // bits of an expert id
+  int rbits;   // bits of a rank id
+  // workspace carve-up (byte offsets from the workspace base)
+  size_t off_hist_e, off_hist_r, off_local_e, off_local_r, off_msg, ws_bytes;
+};
+
+int make_geometry(const ep_problem* p, Geometry* g);  // EP_OK or EP_ERR_*
+
+struct LayoutArgs {
+  Geometry g;
+  int mode, align;
+  const int32_t* topk;
+  int32_t* cnt_rank;       // [R][R]
+  int32_t* cnt_expert;     // [R][E]
+  uint8_t* in_rank;        // [R][T][R]
+  int32_t* rpm;            // [R][R]
+  int32_t* recv_per_expert;// [E]
+  int32_t* expert_start;   // [E]
+  int32_t* rows;           // [R]
+  int32_t* row_base;       // [R+1]
+  int32_t* send_pos;       // [R][T][K] or NULL
+  int32_t* send_head;      // [R][T][R] or NULL
+  int32_t* recv_src_idx;   // or NULL
+  int64_t recv_cap;
+  int32_t* err;
+  // workspace
+  int32_t* hist_e;         // [E][NC]
+  int32_t* hist_r;         // [R][R][C]
+  int32_t* local_e;        // [R][T][K]
+  int32_t* local_r;        // [R][T][R]
+};
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+struct DispatchArgs {
+  Geometry g;
+  int mode, quant;
+  const uint16_t* x;
+  const int32_t* send_pos;
+  void* recv_x;
+  void* recv_scales;
+  int64_t cap;
+  int32_t* err;
+};
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  Geometry g;
+  const uint16_t* y;
+  int64_t y_rows;
+  const int32_t* send_pos;
+  const float* w;
+  uint16_t* out;
+  int32_t* err;
+};
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+struct MessageArgs {
+  Geometry g;
+  int quant;
+  int64_t region_bytes;
+  uint32_t epoch;
+  const uint16_t* x;
+  const int32_t* topk;
+  const float* w;
+  const int32_t* cnt_rank;   // [R][R]
+  const int32_t* send_head;  // [R][T][R]
+  uint8_t* arena;
+  int64_t arena_cap;
+  int64_t* table;            // [R][R][8]
+  int64_t* arena_base;       // [2][R+1]
+  uint8_t* desc;
+  int64_t desc_cap;
+  int64_t* num_desc;
+  int32_t* err;
+  void* ws;                  // message workspace
+};
+
+hipError_t launch_messages(const MessageArgs& a, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,278 @@
+// Routing layout on gfx950: per-rank / per-expert histograms, the rank
+// prefix matrix, receive offsets and deterministic slots.
+//
+// "DeepEP" deep dive (llm-infra-atlas, moe/06_deepep), sec. 2.1 (counts,
+// rank prefix matrix, expert_alignment), sec. 2.3 (send_head /
+// recv_src_idx address book), sec. 3.2 (rank of an expert), sec. 4.3
+// (per-expert prefix sums as segment offsets).
+//
+// Four launches, all small next to the data movement they enable:
+//   1. count   : one wavefront per token chunk.  Entries of a batch (one per
+//                lane, in (token, k) order) find their equal-key peers with
+//                one ballot per key bit; the lowest lane of each key advances
+//                that key's counter in LDS.  This gives every entry its rank
+//                among same-expert entries of the chunk, and every first hit
+//                of a token on a rank its rank among the chunk's tokens sent
+//                there.  No atomics decide positions: slots are deterministic.
+//   2. scan    : one block per expert (chunk histogram -> exclusive prefix
+//                over (source rank, chunk)) and one per destination rank
+//                (token counts, the rank prefix matrix column, chunk prefixes).
+//   3. offsets : one block: segment starts (prefix of aligned counts), rows
+//                per rank, row bases, padding rows.
+//   4. finalize: slot = segment start + chunk prefix + rank in chunk.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+
+namespace ep {
+
+constexpr int kLayoutWaves = 4;  // most wavefronts (chunks) per count block
+
+__global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
+  extern __shared__ int32_t smem[];
+  const Geometry& g = a.g;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (chunk >= g.NC) return;  // uniform per wave
+  const int per_wave = g.E + g.R + g.tb * g.R;
+  int32_t* cnt_e = smem + wave * per_wave;
+  int32_t* cnt_r = cnt_e + g.E;
+  int32_t* rowbuf = cnt_r + g.R;
+  for (int i = lane; i < g.E + g.R; i += kWave) cnt_e[i] = 0;
+
+  const int s = chunk / g.C, c = chunk % g.C;
+  const int t_begin = c * g.ct;
+  const int t_end = min(g.T, t_begin + g.ct);
+  const int K = g.K;
+  const int my_tok = lane / K, my_k = lane % K;
+  const int nent = g.tb * K;
+  // lanes of my own token below me
+  const int first_lane = my_tok * K;
+  const uint64_t below = lanes_below();
+  const uint64_t own_below = below & ~(first_lane == 0 ? 0ull : (~0ull >> (64 - first_lane)));
+
+  for (int t0 = t_begin; t0 < t_end; t0 += g.tb) {
+    const int t = t0 + my_tok;
+    const bool in_batch = lane < nent && t < t_end;
+    const int64_t ent = ((int64_t)s * g.T + t) * K + my_k;
+    int e = -1;
+    if (in_batch) e = a.topk[ent];
+    const bool valid = in_batch && e >= 0 && e < g.E;
+    const uint64_t vmask = __ballot(valid);
+
+    // expert level: rank among same-expert entries of this chunk
+    const uint64_t eq = match_key(valid ? (uint32_t)e : 0u, g.ebits, vmask);
+    int slot = -1;
+    if (valid) {
+      slot = cnt_e[e] + rank_below(eq);
+      if ((eq & below) == 0) cnt_e[e] = slot + (int)__popcll(eq);
+    }
+    if (in_batch) a.local_e[ent] = slot;
+
+    // rank level: first entry of a token on each rank, and that token's
+    // rank among the chunk's tokens sent to the rank
+    const int r = valid ? e / g.L : 0;
+    const uint64_t eqr = match_key((uint32_t)r, g.rbits, vmask);
+    const bool first = valid && (eqr & own_below) == 0;
+    const uint64_t eqf = eqr & __ballot(first);
+    for (int i = lane; i < g.tb * g.R; i += kWave) rowbuf[i] = -1;
+    if (first) {
+      const int h = cnt_r[r] + rank_below(eqf);
+      rowbuf[my_tok * g.R + r] = h;
+      if ((eqf & below) == 0) cnt_r[r] = h + (int)__popcll(eqf);
+    }
+    const int nt = min(g.tb, t_end - t0);
+    const int64_t rbase = ((int64_t)s * g.T + t0) * g.R;
+    for (int i = lane; i < nt * g.R; i += kWave) {
+      const int v = rowbuf[i];
+      a.in_rank[rbase + i] = v >= 0 ? 1 : 0;
+      a.local_r[rbase + i] = v;
+    }
+  }
+  for (int e = lane; e < g.E; e += kWave) a.hist_e[(int64_t)e * g.NC + chunk] = cnt_e[e];
+  for (int d = lane; d < g.R; d += kWave) a.hist_r[(int64_t)d * g.NC + chunk] = cnt_r[d];
+}
+
+// Exclusive block scan of one int per thread (up to 1024 threads); returns
+// the exclusive prefix, *total receives the block sum.
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  const int nw = blockDim.x >> 6;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) before += wsum[w];
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Exclusive scan, in place, of a row of n = nseg * seg ints; seg_start[j]
+// (LDS) receives the prefix at the start of segment j and seg_start[nseg]
+// the total.  With `relative`, each element is then made relative to its
+// segment's start.
+__device__ void scan_row_segments(int32_t* row, int nseg, int seg, int* seg_start, bool relative) {
+  const int n = nseg * seg;
+  for (int j = threadIdx.x; j <= nseg; j += blockDim.x) seg_start[j] = 0;  // empty rows
+  __syncthreads();
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += row[i];
+  int total;
+  int run = block_exclusive_scan(sum, &total);
+  for (int i = lo; i < hi; ++i) {
+    const int v = row[i];
+    row[i] = run;
+    if (i % seg == 0) seg_start[i / seg] = run;
+    run += v;
+  }
+  if (threadIdx.x == 0) seg_start[nseg] = total;
+  __syncthreads();
+  if (relative)
+    for (int i = lo; i < hi; ++i) row[i] -= seg_start[i / seg];
+}
+
+// Blocks [0, E): expert e's chunk histogram over (source, chunk) becomes
+// its exclusive prefix = rows of earlier sources and chunks; per-source
+// counts and the expert's receive total fall out of the segment starts.
+// Blocks [E, E+R): destination d's token histogram over (source, chunk):
+// per-source totals (num_tokens_per_rank), the inclusive prefix over
+// sources (rank_prefix_matrix column d), and per-source chunk prefixes.
+__global__ __launch_bounds__(256) void layout_scan(LayoutArgs a) {
+  __shared__ int seg_start[257];
+  const Geometry& g = a.g;
+  const int b = blockIdx.x;
+  // errors are raised only by the finalize launch that follows
+  if (b == 0 && threadIdx.x == 0) *a.err = 0;
+  if (b < g.E) {
+    const int e = b;
+    scan_row_segments(a.hist_e + (int64_t)e * g.NC, g.R, g.C, seg_start, false);
+    for (int s = threadIdx.x; s < g.R; s += blockDim.x)
+      a.cnt_expert[(int64_t)s * g.E + e] = seg_start[s + 1] - seg_start[s];
+    if (threadIdx.x == 0) a.recv_per_expert[e] = seg_start[g.R];
+  } else {
+    const int d = b - g.E;
+    scan_row_segments(a.hist_r + (int64_t)d * g.NC, g.R, g.C, seg_start, true);
+    for (int s = threadIdx.x; s < g.R; s += blockDim.x) {
+      a.cnt_rank[s * g.R + d] = seg_start[s + 1] - seg_start[s];
+      a.rpm[s * g.R + d] = seg_start[s + 1];
+    }
+  }
+}
+
+// One block: segment starts, rows per rank, row bases, padding rows.
+__global__ __launch_bounds__(1024) void layout_offsets(LayoutArgs a) {
+  __shared__ int start_lds[2049];
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x;
+  if (a.mode == EP_MODE_LOW_LATENCY) {
+    const int rt = g.R * g.T;
+    for (int e = tid; e < g.E; e += blockDim.x) a.expert_start[e] = e * rt;
+    for (int d = tid; d <= g.R; d += blockDim.x) {
+      if (d < g.R) a.rows[d] = g.L * rt;
+      a.row_base[d] = d * g.L * rt;
+    }
+    return;
+  }
+  // normal (and message) mode: counts rounded up to expert_alignment,
+  // segments back to back in expert order (= rank d, then local expert l)
+  const int per = (g.E + blockDim.x - 1) / blockDim.x;
+  const int lo = min(g.E, tid * per), hi = min(g.E, lo + per);
+  int sum = 0;
+  for (int e = lo; e < hi; ++e) {
+    const int n = a.recv_per_expert[e];
+    sum += (n + a.align - 1) / a.align * a.align;
+  }
+  int total;
+  int run = block_exclusive_scan(sum, &total);
+  for (int e = lo; e < hi; ++e) {
+    const int n = a.recv_per_expert[e];
+    const int nal = (n + a.align - 1) / a.align * a.align;
+    a.expert_start[e] = run;
+    start_lds[e] = run;
+    if (a.recv_src_idx) {
+      for (int r = run + n; r < run + nal; ++r)
+        if (r < a.recv_cap) a.recv_src_idx[r] = -1;
+    }
+    run += nal;
+  }
+  if (tid == 0) start_lds[g.E] = total;
+  __syncthreads();
+  for (int d = tid; d <= g.R; d += blockDim.x) {
+    a.row_base[d] = start_lds[d * g.L];
+    if (d < g.R) a.rows[d] = start_lds[(d + 1) * g.L] - start_lds[d * g.L];
+  }
+}
+
+__global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
+  const Geometry& g = a.g;
+  const int64_t n_ent = (int64_t)g.R * g.T * g.K;
+  const int64_t n_head = (int64_t)g.R * g.T * g.R;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int rt = g.R * g.T;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_ent; i += stride) {
+    const int e = a.topk[i];
+    if (e < -1 || e >= g.E) set_err(a.err, EP_DEVERR_TOPK_RANGE);
+    const int local = a.local_e[i];
+    int row = -1;
+    if (local >= 0) {
+      const int64_t st = i / g.K;  // s * T + t
+      const int s = (int)(st / g.T), t = (int)(st % g.T);
+      const int pos = a.hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
+      if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
+        set_err(a.err, EP_DEVERR_LL_OVERFLOW);
+      } else {
+        row = a.expert_start[e] + pos;
+        if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
+          if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
+          else set_err(a.err, EP_DEVERR_CAPACITY);
+        }
+      }
+    }
+    if (a.send_pos) a.send_pos[i] = (a.mode == EP_MODE_MESSAGES) ? -1 : row;
+  }
+  if (a.send_head) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_head; i += stride) {
+      int v = a.local_r[i];
+      if (v >= 0) {
+        const int64_t st = i / g.R;
+        const int d = (int)(i % g.R);
+        const int s = (int)(st / g.T), t = (int)(st % g.T);
+        v += a.hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
+      }
+      a.send_head[i] = v;
+    }
+  }
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+  const Geometry& g = a.g;
+  // LDS per wavefront: expert and rank counters plus one batch of rows;
+  // at most 64 KiB per block
+  const size_t per_wave = sizeof(int32_t) * (size_t)(g.E + g.R + g.tb * g.R);
+  int waves = (int)(65536 / per_wave);
+  if (waves > kLayoutWaves) waves = kLayoutWaves;
+  if (waves < 1) waves = 1;
+  const int nb = (g.NC + waves - 1) / waves;
+  if (nb > 0)
+    hipLaunchKernelGGL(layout_count, dim3(nb), dim3(64 * waves), per_wave * waves, stream, a);
+  hipLaunchKernelGGL(layout_scan, dim3(g.E + g.R), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(layout_offsets, dim3(1), dim3(1024), 0, stream, a);
+  const int64_t work = (int64_t)g.R * g.T * (g.K > g.R ? g.K : g.R);
+  int64_t fb = (work + 255) / 256;
+  if (fb > 4096) fb = 4096;
+  if (fb < 1) fb = 1;
+  hipLaunchKernelGGL(layout_finalize, dim3((unsigned)fb), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,325 @@
+"""Thin ctypes binding of libep (include/ep.h): argument marshalling only.
+
+Every step runs in the HIP library; this module turns torch tensors into
+device pointers, fills the C structs, passes the current HIP stream and
+raises ``EPError`` on a non-zero status.  It loads ``libep.so`` from the
+package directory and raises if the library has not been built (there is
+no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep.so")
+
+MODE_NORMAL, MODE_LOW_LATENCY, MODE_MESSAGES = 0, 1, 2
+QUANT_NONE, QUANT_FP8_F32, QUANT_FP8_UE8M0 = 0, 1, 2
+DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY = 1, 2, 4
+
+EXPORTS = ["ep_workspace_bytes", "ep_max_recv_rows", "ep_get_layout", "ep_dispatch",
+           "ep_combine", "ep_status_string"]
+
+
+class EPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class CProblem(ctypes.Structure):
+    _fields_ = [("num_ranks", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_topk", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("quant", ctypes.c_int32),
+                ("region_bytes", ctypes.c_int64), ("epoch", ctypes.c_uint32),
+                ("reserved", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [("num_tokens_per_rank", _vp), ("num_tokens_per_expert", _vp),
+                ("is_token_in_rank", _vp), ("rank_prefix_matrix", _vp),
+                ("recv_tokens_per_expert", _vp), ("expert_start", _vp),
+                ("rows_per_rank", _vp), ("row_base", _vp), ("send_pos", _vp),
+                ("send_head", _vp), ("recv_src_idx", _vp), ("recv_capacity", ctypes.c_int64),
+                ("err", _vp)]
+
+
+class CRecv(ctypes.Structure):
+    _fields_ = [("x", _vp), ("scales", _vp), ("capacity", ctypes.c_int64)]
+
+
+class CMessages(ctypes.Structure):
+    _fields_ = [("send_arena", _vp), ("send_capacity", ctypes.c_int64), ("table", _vp),
+                ("arena_base", _vp), ("descriptors", _vp), ("desc_capacity", ctypes.c_int64),
+                ("num_descriptors", _vp)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run combine_ep_get_layout_amd/build.py")
+        l = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(CProblem)
+        l.ep_workspace_bytes.argtypes = [P]
+        l.ep_workspace_bytes.restype = ctypes.c_size_t
+        l.ep_max_recv_rows.argtypes = [P]
+        l.ep_max_recv_rows.restype = ctypes.c_int64
+        l.ep_get_layout.argtypes = [P, _vp, ctypes.POINTER(CLayout), _vp, ctypes.c_size_t, _vp]
+        l.ep_get_layout.restype = ctypes.c_int
+        l.ep_dispatch.argtypes = [P, ctypes.POINTER(CLayout), _vp, _vp, _vp,
+                                  ctypes.POINTER(CRecv), ctypes.POINTER(CMessages), _vp,
+                                  ctypes.c_size_t, _vp]
+        l.ep_dispatch.restype = ctypes.c_int
+        l.ep_combine.argtypes = [P, ctypes.POINTER(CLayout), _vp, ctypes.c_int64, _vp, _vp, _vp]
+        l.ep_combine.restype = ctypes.c_int
+        l.ep_status_string.argtypes = [ctypes.c_int]
+        l.ep_status_string.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ep_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise EPError(status, what)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libep takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libep takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Problem:
+    R: int
+    T: int
+    H: int
+    E: int
+    K: int
+    align: int = 1
+    mode: int = MODE_NORMAL
+    quant: int = QUANT_NONE
+    region_bytes: int = 2 << 20
+    epoch: int = 1
+
+    def c(self) -> CProblem:
+        return CProblem(self.R, self.T, self.H, self.E, self.K, self.align, self.mode, self.quant,
+                        self.region_bytes, self.epoch, 0)
+
+    @property
+    def L(self) -> int:
+        return self.E // self.R
+
+    @property
+    def G(self) -> int:
+        return self.H // 128
+
+
+def workspace_bytes(p: Problem) -> int:
+    return int(lib().ep_workspace_bytes(ctypes.byref(p.c())))
+
+
+def max_recv_rows(p: Problem) -> int:
+    return int(lib().ep_max_recv_rows(ctypes.byref(p.c())))
+
+
+class Layout:
+    """Device buffers of one ep_get_layout call (the dispatch handle)."""
+
+    def __init__(self, p: Problem, device="cuda", recv_capacity: int | None = None,
+                 send_head: bool = True, recv_src_idx: bool = True):
+        R, T, E, K = p.R, p.T, p.E, p.K
+        i32 = dict(dtype=torch.int32, device=device)
+        self.num_tokens_per_rank = torch.empty((R, R), **i32)
+        self.num_tokens_per_expert = torch.empty((R, E), **i32)
+        self.is_token_in_rank = torch.empty((R, T, R), dtype=torch.uint8, device=device)
+        self.rank_prefix_matrix = torch.empty((R, R), **i32)
+        self.recv_tokens_per_expert = torch.empty(E, **i32)
+        self.expert_start = torch.empty(E, **i32)
+        self.rows_per_rank = torch.empty(R, **i32)
+        self.row_base = torch.empty(R + 1, **i32)
+        self.send_pos = torch.empty((R, T, K), **i32) if p.mode != MODE_MESSAGES else None
+        need_head = send_head or p.mode == MODE_MESSAGES
+        self.send_head = torch.empty((R, T, R), **i32) if need_head else None
+        if recv_capacity is None:
+            recv_capacity = max_recv_rows(p) if p.mode != MODE_MESSAGES else 0
+        self.recv_capacity = int(recv_capacity)
+        self.recv_src_idx = (torch.empty(max(self.recv_capacity, 1), **i32)
+                             if recv_src_idx and p.mode != MODE_MESSAGES else None)
+        self.err = torch.zeros(1, **i32)
+
+    def c(self) -> CLayout:
+        return CLayout(_ptr(self.num_tokens_per_rank), _ptr(self.num_tokens_per_expert),
+                       _ptr(self.is_token_in_rank), _ptr(self.rank_prefix_matrix),
+                       _ptr(self.recv_tokens_per_expert), _ptr(self.expert_start),
+                       _ptr(self.rows_per_rank), _ptr(self.row_base), _ptr(self.send_pos),
+                       _ptr(self.send_head), _ptr(self.recv_src_idx),
+                       self.recv_capacity if self.recv_src_idx is not None else 0,
+                       _ptr(self.err))
+
+
+def workspace(p: Problem, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(p)
+    if n == 0:
+        raise EPError(-3, "workspace size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _need(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def get_layout(p: Problem, topk_idx: torch.Tensor, layout: Layout, ws: torch.Tensor,
+               stream=None) -> None:
+    R, T, E, K = p.R, p.T, p.E, p.K
+    _need(topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32")
+    _need(layout.num_tokens_per_expert.numel() == R * E and layout.is_token_in_rank.numel() == R * T * R,
+          "layout buffers do not match the problem")
+    _need(layout.send_pos is None or layout.send_pos.numel() == R * T * K, "send_pos [R][T][K]")
+    _need(layout.send_head is None or layout.send_head.numel() == R * T * R, "send_head [R][T][R]")
+    _need(layout.recv_src_idx is None or layout.recv_src_idx.numel() >= layout.recv_capacity,
+          "recv_src_idx smaller than recv_capacity")
+    _need(ws.numel() >= workspace_bytes(p), "workspace too small")
+    cl = layout.c()
+    _check(lib().ep_get_layout(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl), _ptr(ws),
+                               ws.numel(), _stream(stream)), "ep_get_layout")
+
+
+class Recv:
+    """Receive buffers of normal / low-latency dispatch."""
+
+    def __init__(self, p: Problem, capacity: int, device="cuda"):
+        self.capacity = int(capacity)
+        if p.quant == QUANT_NONE:
+            self.x = torch.empty((self.capacity, p.H), dtype=torch.bfloat16, device=device)
+            self.scales = None
+        else:
+            self.x = torch.empty((self.capacity, p.H), dtype=torch.uint8, device=device)
+            n = p.G * (p.E * p.R * p.T if p.mode == MODE_LOW_LATENCY else self.capacity)
+            dt = torch.float32 if p.quant == QUANT_FP8_F32 else torch.uint8
+            self.scales = torch.empty(max(n, 1), dtype=dt, device=device)
+
+    def c(self) -> CRecv:
+        return CRecv(_ptr(self.x), _ptr(self.scales), self.capacity)
+
+
+class Messages:
+    """Send arena, per-message table and descriptors of message mode."""
+
+    def __init__(self, p: Problem, send_capacity: int, desc_capacity: int, device="cuda"):
+        R = p.R
+        self.send_capacity = int(send_capacity)
+        self.desc_capacity = int(desc_capacity)
+        self.send_arena = torch.empty(max(self.send_capacity, 16), dtype=torch.uint8,
+                                      device=device)
+        self.table = torch.empty((R, R, 8), dtype=torch.int64, device=device)
+        self.arena_base = torch.empty((2, R + 1), dtype=torch.int64, device=device)
+        self.descriptors = torch.empty((max(self.desc_capacity, 1), 64), dtype=torch.uint8,
+                                       device=device)
+        self.num_descriptors = torch.zeros(1, dtype=torch.int64, device=device)
+
+    def c(self) -> CMessages:
+        return CMessages(_ptr(self.send_arena), self.send_capacity, _ptr(self.table),
+                         _ptr(self.arena_base), _ptr(self.descriptors), self.desc_capacity,
+                         _ptr(self.num_descriptors))
+
+
+def dispatch(p: Problem, layout: Layout, x: torch.Tensor, *, recv: Recv | None = None,
+             msgs: Messages | None = None, topk_idx: torch.Tensor | None = None,
+             topk_weights: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+             stream=None) -> None:
+    R, T, H, E, K = p.R, p.T, p.H, p.E, p.K
+    _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
+    if p.mode != MODE_MESSAGES:
+        _need(recv is not None and layout.send_pos is not None, "recv buffers and send_pos")
+        _need(recv.x.shape[0] >= recv.capacity and recv.x.shape[1] == H, "recv x [capacity][H]")
+        if p.quant != QUANT_NONE:
+            n = p.G * (E * R * T if p.mode == MODE_LOW_LATENCY else recv.capacity)
+            _need(recv.scales is not None and recv.scales.numel() >= n, "recv scales")
+            _need(recv.x.element_size() == 1, "FP8 codes are bytes")
+        else:
+            _need(recv.x.element_size() == 2, "bf16 rows")
+    else:
+        _need(msgs is not None and layout.send_head is not None, "message buffers and send_head")
+        _need(topk_idx is not None and topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K,
+              "topk_idx [R][T][K] int32")
+        _need(topk_weights is not None and topk_weights.dtype == torch.float32
+              and topk_weights.numel() == R * T * K, "topk_weights [R][T][K] fp32")
+        _need(msgs.send_arena.numel() >= msgs.send_capacity, "send arena")
+        _need(msgs.descriptors.shape[0] >= msgs.desc_capacity, "descriptors")
+        _need(ws is not None and ws.numel() >= workspace_bytes(p), "workspace too small")
+    cl = layout.c()
+    cr = recv.c() if recv is not None else None
+    cm = msgs.c() if msgs is not None else None
+    _check(lib().ep_dispatch(ctypes.byref(p.c()), ctypes.byref(cl), _ptr(x), _ptr(topk_idx),
+                             _ptr(topk_weights), ctypes.byref(cr) if cr is not None else None,
+                             ctypes.byref(cm) if cm is not None else None, _ptr(ws),
+                             ws.numel() if ws is not None else 0, _stream(stream)),
+           "ep_dispatch")
+
+
+def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,
+            out: torch.Tensor, stream=None) -> None:
+    R, T, H, K = p.R, p.T, p.H, p.K
+    _need(y.dtype == torch.bfloat16 and y.dim() == 2 and y.shape[1] == H, "y [rows][H] bf16")
+    _need(topk_weights.dtype == torch.float32 and topk_weights.numel() == R * T * K,
+          "topk_weights [R][T][K] fp32")
+    _need(out.dtype == torch.bfloat16 and out.numel() == R * T * H, "out [R][T][H] bf16")
+    _need(layout.send_pos is not None and layout.send_pos.numel() == R * T * K, "send_pos")
+    cl = layout.c()
+    y_rows = y.shape[0]
+    _check(lib().ep_combine(ctypes.byref(p.c()), ctypes.byref(cl), _ptr(y), y_rows,
+                            _ptr(topk_weights), _ptr(out), _stream(stream)), "ep_combine")
+
+
+def messages_capacity(p: Problem, counts=None) -> tuple[int, int]:
+    """(send bytes, descriptors) that suffice.  With per-(s,d) token counts
+    (host [R][R]) the bound is tight to within the arena alignment; without,
+    it is the worst case (every token to every rank)."""
+    import numpy as np
+
+    R, T, H, K, G = p.R, p.T, p.H, p.K, p.G
+    cb = 2 if p.quant == QUANT_NONE else 1
+    sb = {QUANT_NONE: 0, QUANT_FP8_F32: 4, QUANT_FP8_UE8M0: 1}[p.quant]
+
+    def pad(v):
+        return (v + 15) // 16 * 16
+
+    def region(n):
+        return 0 if n == 0 else 32 + pad(n * H * cb) + pad(n * G * sb) + 2 * pad(n * K * 4) + pad(n * 4)
+
+    rb = p.region_bytes
+    if counts is None:
+        counts = np.full((R, R), T, np.int64)
+    sizes = np.vectorize(region)(np.asarray(counts, np.int64))
+    send = int(sum((s + rb - 1) // rb * rb for s in sizes.sum(axis=1)))
+    # chunks per put <= 1 + crossings on either side
+    desc = int(sum(3 + 2 * ((r // rb) + 2) for r in sizes.reshape(-1) if r > 0))
+    return max(send, 16), max(desc, 1)

@@ -110,10 +110,12 @@ def gen_x(w: Workload) -> np.ndarray:
     if w.outlier_frac > 0:
         nout = int(round(w.outlier_frac * w.H))
         cols = rs.choice(w.H, size=nout, replace=False)
-    chunk = max(1, (1 << 24) // w.H)
+    chunk = max(1, (1 << 22) // w.H)
+    buf = np.empty((chunk, w.H), np.float32)
     for i in range(0, n, chunk):
         j = min(n, i + chunk)
-        a = rx.standard_normal((j - i, w.H), dtype=np.float32)
+        a = buf[: j - i]
+        rx.standard_normal(out=a, dtype=np.float32)
         if cols is not None:
             a[:, cols] *= np.float32(w.outlier_scale)
         out[i:j] = f32_to_bf16_bits(a)

@@ -1,0 +1,203 @@
+/*
+ * ep.h -- C ABI of libep: MoE token dispatch / combine on simulated ranks
+ * that live as partitions of one MI355X's HBM (gfx950).
+ *
+ * The method (web pages it is described on):
+ *   "DeepEP" deep dive (llm-infra-atlas, moe/06_deepep)
+ *     sec. 1.1  normal mode: contiguous per-expert receive layout, FP8
+ *               dispatch with bf16 combine, receive size known only after
+ *               the count exchange (or a worst-case capacity);
+ *     sec. 1.2  low-latency mode: packed masked layout
+ *               [local experts][max tokens per rank * ranks][hidden] plus a
+ *               per-expert receive count; FP8 scales fp32 or power of two
+ *               (UE8M0), column-major;
+ *     sec. 2.1  get_dispatch_layout counts (tokens per rank, per expert,
+ *               is_token_in_rank) and notify_dispatch (prefix sum over
+ *               source ranks = rank_prefix_matrix; per-expert receive
+ *               counts rounded up to expert_alignment);
+ *     sec. 2.3  rank_prefix_matrix[i][j] = tokens sent to rank j by ranks
+ *               <= i; the handle (send_head, recv_src_idx) lets combine walk
+ *               dispatch's addresses backwards;
+ *     sec. 3.2  destination rank of expert e = e / num_local_experts;
+ *     sec. 4.3  psum of per-expert receive counts = segment offsets.
+ *   "Eaas_server" notes: 16-byte aligned per-destination message with a
+ *     header, then payload, then a completion flag; only loaded
+ *     destinations get one; three puts (payload, header, flag).
+ *   "ibgda_device.cuh" notes, sec. 1 and 3: a write is cut so that no
+ *     piece spans two memory regions; a write work-queue entry is a
+ *     control, a remote-address and a data segment, big-endian fields.
+ *   "GPU-Initiated Communication: Dissecting Down to the Bone", WQE
+ *     anatomy: 16-byte segments in 64-byte basic blocks.
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller, 16-byte
+ *    aligned unless stated.  Struct arguments themselves are host memory,
+ *    read during the call only.  The library allocates nothing, keeps no
+ *    state between calls and is reentrant; calls that write the same
+ *    buffers must not overlap.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *    enqueued asynchronously on it; nothing is synchronised.
+ *  - Return: EP_OK (0) or a negative EP_ERR_* code.  Argument errors are
+ *    detected on the host before anything is enqueued.  Errors that depend
+ *    on device data (an expert id out of range, a capacity overflow) set
+ *    bits in the caller's device error word (EP_DEVERR_*) and the offending
+ *    write is skipped; read the word after synchronising.
+ *  - Sizes: R = num_ranks, T = num_tokens (per rank), H = hidden,
+ *    E = num_experts, K = num_topk, L = E / R, G = H / 128.
+ *    Limits: 1 <= R <= 256, E % R == 0, E <= 2048, 1 <= K <= 64, T >= 1,
+ *    H % 8 == 0 (bf16 rows are whole 16-byte vectors), H % 128 == 0 when
+ *    quantised, R*T*K < 2^31, receive rows < 2^31.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* receive layouts */
+#define EP_MODE_NORMAL 0      /* contiguous, expert-major per destination rank */
+#define EP_MODE_LOW_LATENCY 1 /* packed masked: E blocks of R*T rows           */
+#define EP_MODE_MESSAGES 2    /* one packed message per (source, destination)  */
+
+/* payload formats */
+#define EP_QUANT_NONE 0      /* bf16 rows                                      */
+#define EP_QUANT_FP8_F32 1   /* e4m3 codes + fp32 scale (amax / 448) per 128 channels */
+#define EP_QUANT_FP8_UE8M0 2 /* e4m3 codes + power-of-two scale stored as a biased 8-bit exponent */
+
+/* host-side status codes */
+#define EP_OK 0
+#define EP_ERR_NULL (-1)        /* a required pointer is NULL              */
+#define EP_ERR_ALIGN (-2)       /* a pointer is not 16-byte aligned        */
+#define EP_ERR_SHAPE (-3)       /* inconsistent or out-of-limit sizes      */
+#define EP_ERR_MODE (-4)        /* unknown mode / quant, or a combination not offered */
+#define EP_ERR_WORKSPACE (-5)   /* workspace smaller than ep_workspace_bytes */
+#define EP_ERR_CAPACITY (-6)    /* a capacity that is too small on its face */
+#define EP_ERR_HIP (-7)         /* the HIP runtime reported a launch error */
+
+/* device error word bits */
+#define EP_DEVERR_TOPK_RANGE 1  /* a topk_idx entry outside [-1, E): entry skipped */
+#define EP_DEVERR_LL_OVERFLOW 2 /* low-latency position >= R*T (duplicate ids): skipped */
+#define EP_DEVERR_CAPACITY 4    /* a row or byte offset past the caller's capacity: skipped */
+
+typedef struct ep_problem {
+  int32_t num_ranks;        /* R                                           */
+  int32_t num_tokens;       /* T, tokens per source rank                   */
+  int32_t hidden;           /* H                                           */
+  int32_t num_experts;      /* E                                           */
+  int32_t num_topk;         /* K                                           */
+  int32_t expert_alignment; /* >= 1; normal mode rounds each expert's rows up to it */
+  int32_t mode;             /* EP_MODE_*                                   */
+  int32_t quant;            /* EP_QUANT_*                                  */
+  int64_t region_bytes;     /* messages: descriptor split granularity (> 0, multiple of 16) */
+  uint32_t epoch;           /* messages: value of the completion flag      */
+  int32_t reserved;         /* must be 0                                   */
+} ep_problem;
+
+/* Outputs of ep_get_layout (the dispatch "handle").  Rows are receive-
+ * buffer rows: normal mode packs the R destination partitions back to
+ * back (partition d = rows [row_base[d], row_base[d+1])), each holding its
+ * L experts' segments in order, each segment ordered by (source rank,
+ * token, k); low-latency mode gives expert e the rows [e*R*T, (e+1)*R*T).
+ * A row index is int32. */
+typedef struct ep_layout {
+  int32_t* num_tokens_per_rank;    /* [R][R]  [s][d]: tokens of s with >= 1 expert on d   */
+  int32_t* num_tokens_per_expert;  /* [R][E]  [s][e]: (token, k) entries of s routed to e  */
+  uint8_t* is_token_in_rank;       /* [R][T][R] 0/1 (any alignment)                        */
+  int32_t* rank_prefix_matrix;     /* [R][R]  [i][j] = sum_{s <= i} num_tokens_per_rank[s][j] */
+  int32_t* recv_tokens_per_expert; /* [E]     entries routed to e (low-latency recv_count) */
+  int32_t* expert_start;           /* [E]     first row of e's segment                      */
+  int32_t* rows_per_rank;          /* [R]     rows of partition d (aligned)                 */
+  int32_t* row_base;               /* [R+1]   first row of partition d; [R] = total rows    */
+  int32_t* send_pos;               /* [R][T][K] row of each entry, -1 if none (normal / LL) */
+  int32_t* send_head;              /* [R][T][R] index of token t in the (s, d) stream in token
+                                      order, -1 if not sent; may be NULL except in messages mode */
+  int32_t* recv_src_idx;           /* [recv_capacity] s*T+t of each filled row; normal mode
+                                      writes -1 in alignment padding rows; may be NULL      */
+  int64_t recv_capacity;           /* rows available in recv_src_idx (and the receive buffer) */
+  int32_t* err;                    /* [1] device error word; ep_get_layout resets it to 0  */
+} ep_layout;
+
+/* Receive side of normal / low-latency dispatch. */
+typedef struct ep_recv {
+  void* x;          /* [capacity][H]: bf16 (EP_QUANT_NONE) or e4m3 codes (1 byte)          */
+  void* scales;     /* FP8 only, column-major: normal [G][capacity];
+                       low-latency [E][G][R*T].  fp32 (FP8_F32) or uint8 exponents
+                       (FP8_UE8M0: scale = 2^(byte - 127)); 4-byte aligned               */
+  int64_t capacity; /* rows of x; low-latency needs >= E*R*T                              */
+} ep_recv;
+
+/* Send side of message mode. */
+typedef struct ep_messages {
+  uint8_t* send_arena;     /* [send_capacity] bytes: all ranks' send arenas, back to back  */
+  int64_t send_capacity;
+  int64_t* table;          /* [R][R][8] per (s, d): send offset, recv offset, region bytes,
+                              token count n, body bytes, first descriptor, descriptor count, 0
+                              (offsets -1 and sizes 0 when n == 0)                         */
+  int64_t* arena_base;     /* [2][R+1]: send-arena bases, then receive-arena bases         */
+  uint8_t* descriptors;    /* [desc_capacity][64] write descriptors                        */
+  int64_t desc_capacity;
+  int64_t* num_descriptors; /* [1] descriptors produced (may exceed the capacity)          */
+} ep_messages;
+
+/* Bytes of scratch device memory ep_get_layout / ep_dispatch need for this
+ * problem (0 on invalid input).  Any 256-byte aligned buffer of at least
+ * this size; its contents need not be initialised and are dead after the
+ * stream reaches the end of the call. */
+size_t ep_workspace_bytes(const ep_problem* p);
+
+/* Worst-case receive rows for normal mode (every entry valid, every
+ * expert padded by expert_alignment - 1), E*R*T for low-latency. */
+int64_t ep_max_recv_rows(const ep_problem* p);
+
+/* Routing layout ("DeepEP" sec. 2.1, 2.3, 3.2, 4.3): histograms per rank
+ * and per expert, is_token_in_rank, the rank prefix matrix, per-expert
+ * receive counts and segment starts, and the slot of every routed entry
+ * (send_pos) and of every sent token within its destination stream
+ * (send_head).  topk_idx: [R][T][K] int32, -1 = no expert.  Slot order is
+ * deterministic: within an expert's segment by (source rank, token, k).
+ * Resets *err to 0, then may set EP_DEVERR_TOPK_RANGE, _LL_OVERFLOW,
+ * _CAPACITY (recv_src_idx too small). */
+int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout* out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch.
+ * normal / low-latency ("DeepEP" sec. 1.1, 1.2): every routed entry
+ *   (s, t, k) writes token x[s][t] to row send_pos[s][t][k] of recv->x,
+ *   as bf16 or as e4m3 codes with one scale per 128-channel group (the
+ *   group's largest magnitude maps to 448; UE8M0 rounds the scale up to a
+ *   power of two).  Uses layout->send_pos; `msgs` may be NULL.
+ * messages ("Eaas_server" notes; "ibgda_device.cuh" sec. 1, 3): for every
+ *   (s, d) with num_tokens_per_rank[s][d] > 0, one region in s's send arena:
+ *   16-byte header {s, d, n, body bytes} (u32 LE), body = codes n*H |
+ *   scales n*G | weights n*K f32 | expert ids n*K i32 | source token n i32,
+ *   each section zero-padded to 16 bytes, then a 16-byte completion flag
+ *   {epoch, 0, 0, 0}, written after the rest of the region.  Then the
+ *   64-byte write descriptors of the payload, header and flag puts, cut at
+ *   every region_bytes boundary of either arena.  Uses layout->send_head,
+ *   num_tokens_per_rank; `recv` may be NULL.
+ * x: [R][T][H] bf16.  topk_idx / topk_weights ([R][T][K]) are read in
+ * messages mode only (may be NULL otherwise). */
+int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
+                const int32_t* topk_idx, const float* topk_weights, const ep_recv* recv,
+                const ep_messages* msgs, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Combine ("DeepEP" sec. 2.3: the handle walked backwards): out[s][t] =
+ * bf16( sum_k topk_weights[s][t][k] * y[send_pos[s][t][k]] ), accumulated in
+ * fp32 in k order, rounded to nearest-even; tokens with no routed entry
+ * get 0.  y: expert outputs, bf16, in the receive layout ([y_rows][H]).
+ * Normal / low-latency modes. */
+int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y,
+               int64_t y_rows, const float* topk_weights, uint16_t* out, void* stream);
+
+/* Static text for a status code. */
+const char* ep_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_H */

@@ -200,14 +200,18 @@ def layout(p: Problem, topk: np.ndarray, recv_cap: int | None = None) -> Layout:
 
 
 # ---------------------------------------------------------------- dispatch
-def dispatch(p: Problem, x: np.ndarray, topk: np.ndarray, send_pos: np.ndarray, cap: int):
+def dispatch(p: Problem, x: np.ndarray, topk: np.ndarray, send_pos: np.ndarray, cap: int,
+             out=None):
     """Returns (err, recv, scales).  recv: uint16 [cap][H] (bf16 bits) or
-    uint8 [cap][H] codes; scales: None, float32 or uint8, column-major."""
+    uint8 [cap][H] codes; scales: None, float32 or uint8, column-major.
+    ``out`` = (recv, scales) preallocated by the caller, else fresh zeros."""
     R, T, H, K, G = p.R, p.T, p.H, p.K, p.G
     x = np.ascontiguousarray(x, dtype=np.uint16).reshape(R, T, H)
     topk = np.ascontiguousarray(topk, dtype=np.int32)
     send_pos = np.ascontiguousarray(send_pos, dtype=np.int32)
-    if p.quant == Q_NONE:
+    if out is not None:
+        recv, scales = out
+    elif p.quant == Q_NONE:
         recv = np.zeros((cap, H), np.uint16)
         scales = None
     else:
@@ -232,20 +236,21 @@ def dequant_rows(p: Problem, codes: np.ndarray, scales: np.ndarray, cap: int,
 
 # ---------------------------------------------------------------- combine
 def combine(p: Problem, y: np.ndarray, w: np.ndarray, send_pos: np.ndarray,
-            tokens: np.ndarray | None = None):
+            tokens: np.ndarray | None = None, out: np.ndarray | None = None):
     """Returns (err, out) with out uint16 bf16 bits: [R][T][H], or
-    [len(tokens)][H] when a flat token list (s*T+t) is given."""
+    [len(tokens)][H] when a flat token list (s*T+t) is given (``out`` may
+    be preallocated by the caller)."""
     y = np.ascontiguousarray(y, dtype=np.uint16)
     w = np.ascontiguousarray(w, dtype=np.float32)
     send_pos = np.ascontiguousarray(send_pos, dtype=np.int32)
     y_rows = y.shape[0] if y.ndim == 2 else y.size // p.H
     if tokens is None:
-        out = np.zeros((p.R, p.T, p.H), np.uint16)
+        out = np.zeros((p.R, p.T, p.H), np.uint16) if out is None else out
         err = lib().orc_combine(ctypes.byref(p.c()), _ptr(y), y_rows, _ptr(w), _ptr(send_pos),
                                 None, 0, _ptr(out))
     else:
         tokens = np.ascontiguousarray(tokens, dtype=np.int64)
-        out = np.zeros((tokens.size, p.H), np.uint16)
+        out = np.zeros((tokens.size, p.H), np.uint16) if out is None else out
         err = lib().orc_combine(ctypes.byref(p.c()), _ptr(y), y_rows, _ptr(w), _ptr(send_pos),
                                 _ptr(tokens), tokens.size, _ptr(out))
     return err, out

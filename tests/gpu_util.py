@@ -1,0 +1,94 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+the CPU oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from combine_ep_get_layout_amd import ep, inputs
+from oracle import oracle as orc
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def problems(w: inputs.Workload, align: int = 1):
+    kw = dict(align=align, mode=w.mode, quant=w.quant, region_bytes=w.region_bytes, epoch=w.epoch)
+    return (ep.Problem(w.R, w.T, w.H, w.E, w.K, **kw),
+            orc.Problem(w.R, w.T, w.H, w.E, w.K, **kw))
+
+
+def gpu_layout(p: ep.Problem, topk: np.ndarray, recv_cap: int | None = None):
+    lay = ep.Layout(p, recv_capacity=recv_cap)
+    ws = ep.workspace(p)
+    ep.get_layout(p, torch.from_numpy(np.ascontiguousarray(topk, np.int32)).to(DEV), lay, ws)
+    torch.cuda.synchronize()
+    return lay, ws
+
+
+def h(t: torch.Tensor | None):
+    return None if t is None else t.cpu().numpy()
+
+
+LAYOUT_FIELDS = ["num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+                 "rank_prefix_matrix", "recv_tokens_per_expert", "expert_start",
+                 "rows_per_rank", "row_base", "send_pos", "send_head"]
+
+
+def assert_layout_equal(gl: ep.Layout, ol: orc.Layout, mode: int):
+    for f in LAYOUT_FIELDS:
+        g = getattr(gl, f)
+        if g is None:
+            continue
+        o = getattr(ol, f)
+        assert np.array_equal(h(g), o), f
+    if gl.recv_src_idx is not None:
+        g = h(gl.recv_src_idx)[: ol.recv_src_idx.size]
+        o = ol.recv_src_idx
+        if mode == ep.MODE_NORMAL:
+            assert np.array_equal(g, o), "recv_src_idx"
+        else:  # low-latency: only rows below each expert's count are defined
+            filled = o >= 0
+            assert np.array_equal(g[filled], o[filled]), "recv_src_idx"
+    assert int(h(gl.err)[0]) == ol.err, ("err", int(h(gl.err)[0]), ol.err)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def combine_close(g: np.ndarray, o: np.ndarray, absw: np.ndarray):
+    """bf16 combine acceptance: |g - o| <= 1e-2 |o| + 2^-16 sum_k |w_k y_k|.
+    The relative term is the tolerance the method is held to (it covers
+    one-ulp bf16 rounding flips, 2^-7); the absolute term covers the fp32
+    rounding of the sum (at most (K+1) 2^-24 sum |w y|) where cancellation
+    makes |o| small.  Returns the max relative error for reporting."""
+    gf, of = bf16_to_f32(g).astype(np.float64), bf16_to_f32(o).astype(np.float64)
+    tol = 1e-2 * np.abs(of) + 2.0 ** -16 * absw
+    bad = np.abs(gf - of) > tol
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5].tolist())
+    nz = np.abs(of) > 0
+    return float((np.abs(gf - of)[nz] / np.abs(of[nz])).max()) if nz.any() else 0.0
+
+
+def abs_weighted_sum(y_rows_f32: np.ndarray, w: np.ndarray, send_pos: np.ndarray,
+                     tokens: np.ndarray | None = None, row_of=None) -> np.ndarray:
+    """sum_k |w_k| |y[row_k]| per (token, channel), for the tolerance."""
+    K = w.shape[-1]
+    sp = send_pos.reshape(-1, K)
+    ww = np.abs(w.reshape(-1, K)).astype(np.float64)
+    toks = np.arange(sp.shape[0]) if tokens is None else tokens
+    out = np.zeros((len(toks), y_rows_f32.shape[1]))
+    for i, t in enumerate(toks):
+        for k in range(K):
+            r = sp[t, k]
+            if r >= 0:
+                rr = r if row_of is None else row_of[r]
+                out[i] += ww[t, k] * np.abs(y_rows_f32[rr].astype(np.float64))
+    return out

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every entry point include/ep.h declares, and rejects bad arguments on the
+host (no kernel is launched for any case here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_layout_amd import ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "ep.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ep.EXPORTS)
+    lib = ep.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_and_rows_for_workloads():
+    from combine_ep_get_layout_amd import inputs
+    for name in inputs.ORDER:
+        w = inputs.WORKLOADS[name]
+        p = ep.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+        assert ep.workspace_bytes(p) > 0
+        if w.mode == ep.MODE_LOW_LATENCY:
+            assert ep.max_recv_rows(p) == w.E * w.R * w.T
+        elif w.mode == ep.MODE_NORMAL:
+            assert ep.max_recv_rows(p) == w.R * w.T * w.K
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(R=8, T=16, H=128, E=250, K=2), False),          # E % R
+    (dict(R=8, T=16, H=100, E=16, K=2), False),           # H % 8
+    (dict(R=8, T=16, H=136, E=16, K=2, quant=1), False),  # H % 128 with FP8
+    (dict(R=8, T=16, H=136, E=16, K=2), True),
+    (dict(R=0, T=16, H=128, E=16, K=2), False),
+    (dict(R=4, T=16, H=128, E=16, K=65), False),
+    (dict(R=4, T=16, H=128, E=4096, K=2), False),
+    (dict(R=4, T=0, H=128, E=16, K=2), True),             # empty input is valid
+    (dict(R=4, T=16, H=128, E=16, K=2, mode=3), False),
+    (dict(R=4, T=16, H=128, E=16, K=2, quant=7), False),
+    (dict(R=4, T=16, H=128, E=16, K=2, align=0), False),
+    (dict(R=4, T=16, H=128, E=16, K=2, mode=2, region_bytes=8), False),
+])
+def test_problem_validation(kw, ok):
+    p = ep.Problem(**kw)
+    assert (ep.workspace_bytes(p) > 0) == ok
+    assert (ep.max_recv_rows(p) >= 0) == ok
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert ep.status_string(s) != "unknown status"
+    assert ep.status_string(-99) == "unknown status"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host pointers only where no GPU exists")
+def test_argument_errors_return_before_launch():
+    lib = ep.lib()
+    p = ep.Problem(2, 8, 128, 8, 2)
+    buf = np.zeros(1 << 16, np.uint8)
+    base = buf.ctypes.data
+    base16 = (base + 15) // 16 * 16
+    cl = ep.CLayout(*([base16] * 11), 0, base16)
+    pc = ctypes.byref(p.c())
+    ws_n = ep.workspace_bytes(p)
+    # NULL topk
+    assert lib.ep_get_layout(pc, None, ctypes.byref(cl), base16, ws_n, None) == -1
+    # misaligned int array
+    bad = ep.CLayout(*([base16 + 1] + [base16] * 10), 0, base16)
+    assert lib.ep_get_layout(pc, base16, ctypes.byref(bad), base16, ws_n, None) == -2
+    # workspace too small
+    assert lib.ep_get_layout(pc, base16, ctypes.byref(cl), base16, ws_n - 1, None) == -5
+    # bad shape
+    pb = ctypes.byref(ep.Problem(2, 8, 128, 7, 2).c())
+    assert lib.ep_get_layout(pb, base16, ctypes.byref(cl), base16, ws_n, None) == -3
+    # low-latency dispatch with too few rows
+    pl = ep.Problem(2, 8, 128, 8, 2, mode=ep.MODE_LOW_LATENCY)
+    rv = ep.CRecv(base16, None, 8 * 2 * 8 - 1)
+    assert lib.ep_dispatch(ctypes.byref(pl.c()), ctypes.byref(cl), base16, None, None,
+                           ctypes.byref(rv), None, None, 0, None) == -6
+    # misaligned x
+    rv = ep.CRecv(base16, None, 8 * 2 * 8)
+    assert lib.ep_dispatch(ctypes.byref(pl.c()), ctypes.byref(cl), base16 + 2, None, None,
+                           ctypes.byref(rv), None, None, 0, None) == -2
+    # combine refuses message mode
+    pm = ep.Problem(2, 8, 128, 8, 2, mode=ep.MODE_MESSAGES)
+    assert lib.ep_combine(ctypes.byref(pm.c()), ctypes.byref(cl), base16, 1, base16, base16,
+                          None) == -4
+    # message dispatch without message buffers
+    assert lib.ep_dispatch(ctypes.byref(pm.c()), ctypes.byref(cl), base16, base16, base16, None,
+                           None, base16, ws_n, None) == -1
