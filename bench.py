@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--no-ll", action="store_true", help="skip the low-latency workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--calib", action="store_true",
+                    help="also run a plain copy of 2^30 bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: simulated ranks are partitions of one "
@@ -262,6 +264,13 @@ def main():
         del rl
         torch.cuda.empty_cache()
 
+    if args.calib:
+        a = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     probe = copy_probe(torch)
     cpu = None if args.no_cpu else cpu_baseline(w, inputs, args.cpu_tokens)
 

@@ -6,56 +6,68 @@
 // walks dispatch's address book backwards; sec. 5: combine is the inverse
 // of dispatch; sec. 1.1: bf16 combine.
 //
-// Work split: one wavefront owns one piece of one output row.  The K row
-// indices and weights are loaded once per wave (one lane each) and read as
-// scalars; each k streams one piece of one receive row with 16-byte loads.
+// Work split: one block per token, one wavefront per piece of the output row
+// (the whole row in flight at once).  The K row indices and weights are
+// loaded once per wave (one lane each) and read as scalars; the receive rows
+// stream in with 16-byte non-temporal loads, eight rows' loads issued before
+// their multiply-adds.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
 namespace ep {
 
-constexpr int kCombineWaves = 4;
+// One block per token, one wavefront per row piece (NV vectors per lane);
+// the K rows are read in groups with all loads of a group issued before its
+// fused multiply-adds (8 rows per group for one vector per lane, fewer for
+// wider pieces so the loads stay in registers).
 
-// Grid: x = token / 4 (one wavefront per token), y = row piece.
 template <int NV>
-__global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y,
-                                                    const int32_t* __restrict__ send_pos,
-                                                    const float* __restrict__ w,
-                                                    u32x4* __restrict__ out, int V, int K,
-                                                    int n_tok, int64_t y_rows, int32_t* err) {
+__global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y,
+                                                     const int32_t* __restrict__ send_pos,
+                                                     const float* __restrict__ w,
+                                                     u32x4* __restrict__ out, int V, int K,
+                                                     int64_t y_rows, int32_t* err) {
   const int lane = threadIdx.x & 63;
-  const int tok = uniform(blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
-  if (tok >= n_tok) return;
-  const int base = blockIdx.y * kWave * NV;
+  const int tok = blockIdx.x;
+  const int base = uniform(threadIdx.x >> 6) * kWave * NV;
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
   const float myw = lane < K ? w[(int64_t)tok * K + lane] : 0.0f;
+  constexpr int kGroup = NV == 1 ? 8 : (NV == 2 ? 4 : 2);
   float acc[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    const int row = __builtin_amdgcn_readlane(myrow, k);
-    if (row < 0) continue;
-    if (row >= y_rows) {
-      if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
-      continue;
-    }
-    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), k));
-    const u32x4* src = y + (int64_t)row * V;
-    u32x4 v[NV];
+  for (int k0 = 0; k0 < K; k0 += kGroup) {
+    u32x4 v[kGroup][NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {  // clamped, so every load is in bounds
-      const int j = min(base + lane + kWave * i, V - 1);
-      v[i] = __builtin_nontemporal_load(src + j);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[i][2 * q] = __builtin_fmaf(wk, bf16_lo(v[i][q]), acc[i][2 * q]);
-        acc[i][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[i][q]), acc[i][2 * q + 1]);
+    for (int kk = 0; kk < kGroup; ++kk) {
+      const int k = k0 + kk;
+      int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
+      if (row >= y_rows) {
+        if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
+        row = -1;
       }
+      const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;  // row 0 stands in, weight 0
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        v[kk][i] = __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kGroup; ++kk) {
+      const int k = k0 + kk;
+      if (k >= K) break;
+      const int row = __builtin_amdgcn_readlane(myrow, k);
+      if (row < 0 || row >= y_rows) continue;
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), k));
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[i][2 * q] = __builtin_fmaf(wk, bf16_lo(v[kk][i][q]), acc[i][2 * q]);
+          acc[i][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[kk][i][q]), acc[i][2 * q + 1]);
+        }
+    }
   }
   u32x4* dst = out + (int64_t)tok * V;
 #pragma unroll
@@ -72,29 +84,24 @@ __global__ __launch_bounds__(256) void combine_rows(const u32x4* __restrict__ y,
 }
 
 template <int NV>
-static void launch_nv(const CombineArgs& a, int V, int npieces, hipStream_t st) {
+static void launch_nv(const CombineArgs& a, int V, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
-  const int blocks = (N + kCombineWaves - 1) / kCombineWaves;
-  hipLaunchKernelGGL(combine_rows<NV>, dim3(blocks, npieces), dim3(256), 0, st,
-                     (const u32x4*)a.y, a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, N, a.y_rows,
-                     a.err);
+  hipLaunchKernelGGL(combine_rows<NV>, dim3(N), dim3(kWave * waves), 0, st, (const u32x4*)a.y,
+                     a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, a.y_rows, a.err);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int64_t N = (int64_t)a.g.R * a.g.T;
   if (N == 0) return hipSuccess;
   const int V = a.g.H / 8;
-  const int npieces = (V + kWave * 8 - 1) / (kWave * 8);
-  const int nv = (V + kWave * npieces - 1) / (kWave * npieces);
+  int nv = 1;
+  while ((V + kWave * nv - 1) / (kWave * nv) > 16) ++nv;
+  const int waves = (V + kWave * nv - 1) / (kWave * nv);
   switch (nv) {
-    case 1: launch_nv<1>(a, V, npieces, st); break;
-    case 2: launch_nv<2>(a, V, npieces, st); break;
-    case 3: launch_nv<3>(a, V, npieces, st); break;
-    case 4: launch_nv<4>(a, V, npieces, st); break;
-    case 5: launch_nv<5>(a, V, npieces, st); break;
-    case 6: launch_nv<6>(a, V, npieces, st); break;
-    case 7: launch_nv<7>(a, V, npieces, st); break;
-    default: launch_nv<8>(a, V, npieces, st); break;
+    case 1: launch_nv<1>(a, V, waves, st); break;
+    case 2: launch_nv<2>(a, V, waves, st); break;
+    case 3: launch_nv<3>(a, V, waves, st); break;
+    default: launch_nv<4>(a, V, waves, st); break;  // hidden <= 32768: nv <= 4
   }
   return hipGetLastError();
 }

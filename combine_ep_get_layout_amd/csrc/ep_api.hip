@@ -15,7 +15,8 @@ using ep::Geometry;
 
 namespace {
 
-constexpr int kBatches = 16;  // batches of entries per layout chunk
+constexpr int kMaxBatches = 16;     // most batches of entries per layout chunk
+constexpr int kTargetChunks = 2048; // enough wavefronts to spread over the chip
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -38,7 +39,7 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   if (p->quant < EP_QUANT_NONE || p->quant > EP_QUANT_FP8_UE8M0) return EP_ERR_MODE;
   if (R < 1 || R > 256 || T < 0 || K < 1 || K > 64) return EP_ERR_SHAPE;
   if (E < R || E > 2048 || E % R != 0) return EP_ERR_SHAPE;
-  if (H < 8 || H % 8 != 0 || H > (1 << 20)) return EP_ERR_SHAPE;
+  if (H < 8 || H % 8 != 0 || H > 32768) return EP_ERR_SHAPE;
   if (p->quant != EP_QUANT_NONE && H % 128 != 0) return EP_ERR_SHAPE;
   if (p->expert_alignment < 1) return EP_ERR_SHAPE;
   const int64_t entries = (int64_t)R * T * K;
@@ -64,7 +65,12 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   if (tb > cap) tb = cap;
   if (tb < 1) tb = 1;
   g->tb = tb;
-  g->ct = tb * kBatches;
+  // fewer, longer chunks only when there are plenty of them
+  const int64_t batches = (int64_t)R * ((T + tb - 1) / tb);
+  int64_t per = (batches + kTargetChunks - 1) / kTargetChunks;
+  if (per < 1) per = 1;
+  if (per > kMaxBatches) per = kMaxBatches;
+  g->ct = tb * (int)per;
   g->C = (T + g->ct - 1) / g->ct;
   g->NC = R * g->C;
   g->ebits = bits_for(E);

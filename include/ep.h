@@ -30,8 +30,10 @@
  *     anatomy: 16-byte segments in 64-byte basic blocks.
  *
  * Conventions for every entry point:
- *  - All array arguments are DEVICE pointers owned by the caller, 16-byte
- *    aligned unless stated.  Struct arguments themselves are host memory,
+ *  - All array arguments are DEVICE pointers owned by the caller.  Row
+ *    buffers (x, receive rows, y, out, send arena, descriptors) must be
+ *    16-byte aligned, other arrays naturally aligned; arrays with one entry
+ *    per token may be NULL when R*T == 0.  Struct arguments themselves are host memory,
  *    read during the call only.  The library allocates nothing, keeps no
  *    state between calls and is reentrant; calls that write the same
  *    buffers must not overlap.
@@ -44,9 +46,10 @@
  *    write is skipped; read the word after synchronising.
  *  - Sizes: R = num_ranks, T = num_tokens (per rank), H = hidden,
  *    E = num_experts, K = num_topk, L = E / R, G = H / 128.
- *    Limits: 1 <= R <= 256, E % R == 0, E <= 2048, 1 <= K <= 64, T >= 1,
- *    H % 8 == 0 (bf16 rows are whole 16-byte vectors), H % 128 == 0 when
- *    quantised, R*T*K < 2^31, receive rows < 2^31.
+ *    Limits: 1 <= R <= 256, R <= E <= 2048, E % R == 0, 1 <= K <= 64,
+ *    T >= 0, 8 <= H <= 32768, H % 8 == 0 (bf16 rows are whole 16-byte
+ *    vectors), H % 128 == 0 when quantised, R*T*K < 2^31, receive rows
+ *    < 2^31.
  */
 #ifndef EP_H
 #define EP_H
@@ -71,7 +74,7 @@ extern "C" {
 /* host-side status codes */
 #define EP_OK 0
 #define EP_ERR_NULL (-1)        /* a required pointer is NULL              */
-#define EP_ERR_ALIGN (-2)       /* a pointer is not 16-byte aligned        */
+#define EP_ERR_ALIGN (-2)       /* a pointer is not suitably aligned       */
 #define EP_ERR_SHAPE (-3)       /* inconsistent or out-of-limit sizes      */
 #define EP_ERR_MODE (-4)        /* unknown mode / quant, or a combination not offered */
 #define EP_ERR_WORKSPACE (-5)   /* workspace smaller than ep_workspace_bytes */
