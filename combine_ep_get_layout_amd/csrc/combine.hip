@@ -51,7 +51,8 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
       const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;  // row 0 stands in, weight 0
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        v[kk][i] = __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1));
+        v[kk][i] = y_rows > 0 ? __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1))
+                              : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int kk = 0; kk < kGroup; ++kk) {
@@ -83,6 +84,84 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
   }
 }
 
+// Two tokens per block, for one vector per lane and K <= 8: the second
+// token's row loads are issued before the first token's multiply-adds, so
+// each wave keeps a full set of loads in flight while it computes.
+constexpr int kPipeK = 8;
+constexpr int kPipeTokens = 2;
+
+__device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, int K, int j,
+                                           int V, int64_t y_rows, u32x4 (&v)[kPipeK]) {
+  if (y_rows == 0) {  // nothing to read; every entry is skipped
+#pragma unroll
+    for (int k = 0; k < kPipeK; ++k) v[k] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kPipeK; ++k) {
+    int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
+    if (row >= y_rows) row = -1;
+    v[k] = __builtin_nontemporal_load(y + (int64_t)(row < 0 ? 0 : row) * V + min(j, V - 1));
+  }
+}
+
+__global__ __launch_bounds__(1024) void combine_rows_pipe(const u32x4* __restrict__ y,
+                                                          const int32_t* __restrict__ send_pos,
+                                                          const float* __restrict__ w,
+                                                          u32x4* __restrict__ out, int V, int K,
+                                                          int n_tok, int64_t y_rows,
+                                                          int32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int j = uniform(threadIdx.x >> 6) * kWave + lane;
+  const int tok0 = blockIdx.x * kPipeTokens;
+  int myrow = lane < K ? send_pos[(int64_t)tok0 * K + lane] : -1;
+  u32x4 a[kPipeK];
+  load_rows8(y, myrow, K, j, V, y_rows, a);
+  for (int r = 0; r < kPipeTokens; ++r) {
+    const int tok = tok0 + r;
+    if (tok >= n_tok) break;
+    const float myw = lane < K ? w[(int64_t)tok * K + lane] : 0.0f;
+    u32x4 b[kPipeK];
+    int nextrow = -1;
+    const bool more = r + 1 < kPipeTokens && tok + 1 < n_tok;
+    if (more) {
+      nextrow = lane < K ? send_pos[(int64_t)(tok + 1) * K + lane] : -1;
+      load_rows8(y, nextrow, K, j, V, y_rows, b);
+    }
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPipeK; ++k) {
+      if (k >= K) break;
+      const int row = __builtin_amdgcn_readlane(myrow, k);
+      if (row < 0) continue;
+      if (row >= y_rows) {
+        if (lane == 0 && j < kWave) set_err(err, EP_DEVERR_CAPACITY);
+        continue;
+      }
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), k));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = __builtin_fmaf(wk, bf16_lo(a[k][q]), acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wk, bf16_hi(a[k][q]), acc[2 * q + 1]);
+      }
+    }
+    if (j < V) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+      __builtin_nontemporal_store(o, out + (int64_t)tok * V + j);
+    }
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < kPipeK; ++k) a[k] = b[k];
+      myrow = nextrow;
+    }
+  }
+}
+
 template <int NV>
 static void launch_nv(const CombineArgs& a, int V, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
@@ -97,6 +176,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   int nv = 1;
   while ((V + kWave * nv - 1) / (kWave * nv) > 16) ++nv;
   const int waves = (V + kWave * nv - 1) / (kWave * nv);
+  if (nv == 1 && a.g.K <= kPipeK) {
+    const int n = (int)N;
+    hipLaunchKernelGGL(combine_rows_pipe, dim3((n + kPipeTokens - 1) / kPipeTokens),
+                       dim3(kWave * waves), 0, st, (const u32x4*)a.y, a.send_pos, a.w,
+                       (u32x4*)a.out, V, a.g.K, n, a.y_rows, a.err);
+    return hipGetLastError();
+  }
   switch (nv) {
     case 1: launch_nv<1>(a, V, waves, st); break;
     case 2: launch_nv<2>(a, V, waves, st); break;

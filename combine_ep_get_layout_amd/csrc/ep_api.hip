@@ -15,8 +15,11 @@ using ep::Geometry;
 
 namespace {
 
-constexpr int kMaxBatches = 16;     // most batches of entries per layout chunk
-constexpr int kTargetChunks = 2048; // enough wavefronts to spread over the chip
+#ifndef EP_LAYOUT_TARGET_CHUNKS
+#define EP_LAYOUT_TARGET_CHUNKS 1024
+#endif
+constexpr int kMaxBatches = 16;  // most batches of entries per layout chunk
+constexpr int kTargetChunks = EP_LAYOUT_TARGET_CHUNKS;  // wavefronts to spread over the chip
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 

@@ -6,7 +6,7 @@
 // recv_src_idx address book), sec. 3.2 (rank of an expert), sec. 4.3
 // (per-expert prefix sums as segment offsets).
 //
-// Four launches, all small next to the data movement they enable:
+// Three launches, all small next to the data movement they enable:
 //   1. count   : one wavefront per token chunk.  Entries of a batch (one per
 //                lane, in (token, k) order) find their equal-key peers with
 //                one ballot per key bit; the lowest lane of each key advances
@@ -17,9 +17,10 @@
 //   2. scan    : one block per expert (chunk histogram -> exclusive prefix
 //                over (source rank, chunk)) and one per destination rank
 //                (token counts, the rank prefix matrix column, chunk prefixes).
-//   3. offsets : one block: segment starts (prefix of aligned counts), rows
-//                per rank, row bases, padding rows.
-//   4. finalize: slot = segment start + chunk prefix + rank in chunk.
+//   3. finalize: every block scans the per-expert counts (rounded up to
+//                expert_alignment) into segment starts in LDS; slot = segment
+//                start + chunk prefix + rank in chunk; block 0 publishes the
+//                starts, rows per rank and row bases.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -169,24 +170,20 @@ __global__ __launch_bounds__(256) void layout_scan(LayoutArgs a) {
   }
 }
 
-// One block: segment starts, rows per rank, row bases, padding rows.
-__global__ __launch_bounds__(1024) void layout_offsets(LayoutArgs a) {
-  __shared__ int start_lds[2049];
+// Segment starts in LDS: start[e] for e in [0, E].  Every block of the
+// finalize launch computes them itself from the per-expert receive counts
+// (an exclusive scan of the counts rounded up to expert_alignment; fixed
+// blocks of R*T rows in low-latency mode).
+__device__ void segment_starts(const LayoutArgs& a, int* start) {
   const Geometry& g = a.g;
-  const int tid = threadIdx.x;
   if (a.mode == EP_MODE_LOW_LATENCY) {
     const int rt = g.R * g.T;
-    for (int e = tid; e < g.E; e += blockDim.x) a.expert_start[e] = e * rt;
-    for (int d = tid; d <= g.R; d += blockDim.x) {
-      if (d < g.R) a.rows[d] = g.L * rt;
-      a.row_base[d] = d * g.L * rt;
-    }
+    for (int e = threadIdx.x; e <= g.E; e += blockDim.x) start[e] = e * rt;
+    __syncthreads();
     return;
   }
-  // normal (and message) mode: counts rounded up to expert_alignment,
-  // segments back to back in expert order (= rank d, then local expert l)
   const int per = (g.E + blockDim.x - 1) / blockDim.x;
-  const int lo = min(g.E, tid * per), hi = min(g.E, lo + per);
+  const int lo = min(g.E, (int)threadIdx.x * per), hi = min(g.E, lo + per);
   int sum = 0;
   for (int e = lo; e < hi; ++e) {
     const int n = a.recv_per_expert[e];
@@ -195,26 +192,35 @@ __global__ __launch_bounds__(1024) void layout_offsets(LayoutArgs a) {
   int total;
   int run = block_exclusive_scan(sum, &total);
   for (int e = lo; e < hi; ++e) {
+    start[e] = run;
     const int n = a.recv_per_expert[e];
-    const int nal = (n + a.align - 1) / a.align * a.align;
-    a.expert_start[e] = run;
-    start_lds[e] = run;
-    if (a.recv_src_idx) {
-      for (int r = run + n; r < run + nal; ++r)
-        if (r < a.recv_cap) a.recv_src_idx[r] = -1;
-    }
-    run += nal;
+    run += (n + a.align - 1) / a.align * a.align;
   }
-  if (tid == 0) start_lds[g.E] = total;
+  if (threadIdx.x == 0) start[g.E] = total;
   __syncthreads();
-  for (int d = tid; d <= g.R; d += blockDim.x) {
-    a.row_base[d] = start_lds[d * g.L];
-    if (d < g.R) a.rows[d] = start_lds[(d + 1) * g.L] - start_lds[d * g.L];
-  }
 }
 
+// Slots: row = segment start + (source, chunk) prefix + rank in chunk, and
+// the token streams' indices.  Block 0 also publishes the segment starts,
+// rows per rank and row bases; padding rows get recv_src_idx = -1.
 __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
+  __shared__ int start[2049];
   const Geometry& g = a.g;
+  segment_starts(a, start);
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < g.E; e += blockDim.x) a.expert_start[e] = start[e];
+    for (int d = threadIdx.x; d <= g.R; d += blockDim.x) {
+      a.row_base[d] = start[d * g.L];
+      if (d < g.R) a.rows[d] = start[(d + 1) * g.L] - start[d * g.L];
+    }
+  }
+  if (a.mode == EP_MODE_NORMAL && a.recv_src_idx && a.align > 1) {
+    for (int e = blockIdx.x; e < g.E; e += gridDim.x) {
+      const int first = start[e] + a.recv_per_expert[e];
+      for (int r = first + (int)threadIdx.x; r < start[e + 1]; r += blockDim.x)
+        if (r < a.recv_cap) a.recv_src_idx[r] = -1;
+    }
+  }
   const int64_t n_ent = (int64_t)g.R * g.T * g.K;
   const int64_t n_head = (int64_t)g.R * g.T * g.R;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
       if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
         set_err(a.err, EP_DEVERR_LL_OVERFLOW);
       } else {
-        row = a.expert_start[e] + pos;
+        row = start[e] + pos;
         if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
           if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
           else set_err(a.err, EP_DEVERR_CAPACITY);
@@ -266,7 +272,6 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (nb > 0)
     hipLaunchKernelGGL(layout_count, dim3(nb), dim3(64 * waves), per_wave * waves, stream, a);
   hipLaunchKernelGGL(layout_scan, dim3(g.E + g.R), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(layout_offsets, dim3(1), dim3(1024), 0, stream, a);
   const int64_t work = (int64_t)g.R * g.T * (g.K > g.R ? g.K : g.R);
   int64_t fb = (work + 255) / 256;
   if (fb > 4096) fb = 4096;

@@ -420,3 +420,18 @@ def test_workload_messages():
     say("messages: pack")
     om = _messages_compare(w, p, po, gl, topk, x, wt, ws)
     say("messages: descriptors", om.num_desc)
+
+
+def test_combine_without_expert_rows_flags_every_entry():
+    """y with zero rows: nothing is read, every routed entry is flagged, and
+    the output is zero."""
+    w = inputs.small("norows", R=2, T=9, H=256, E=8, K=3, seed=8)
+    topk = inputs.gen_topk(w)
+    p, _ = problems(w)
+    gl, _ = gpu_layout(p, topk)
+    out = torch.full((w.R, w.T, w.H), 3.0, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((0, w.H), dtype=torch.bfloat16, device=DEV)
+    ep.combine(p, gl, y, torch.from_numpy(inputs.gen_weights(w)).to(DEV), out)
+    torch.cuda.synchronize()
+    assert int(h(gl.err)[0]) & ep.DEVERR_CAPACITY
+    assert (out.float() == 0).all().item()
