@@ -1,23 +1,28 @@
 """Benchmark: MoE dispatch + combine on simulated ranks, one MI355X.
 
-One step = one pass of the whole path over one batch: routing layout
-(counts, rank prefix matrix, slots), dispatch scatter into the receive
-layout, combine gather-reduce back to token order.  The expert between
-dispatch and combine is the identity (combine reads the receive buffer),
-so the step moves exactly the path's own bytes.
+One step = one pass of the whole path over one batch: the routing layout
+(counts, rank prefix matrix, slots), the dispatch scatter into the receive
+layout, and the combine gather-reduce back to token order.  The expert
+between dispatch and combine is the identity for bf16 layouts (combine
+reads the receive buffer), so the step moves exactly the path's own bytes;
+FP8 layouts combine bf16 expert outputs of the receive shape.  In message
+mode a step is the layout plus the packer (table, payload, header / flag /
+descriptors).
 
-Default workload: 8 simulated ranks x 4096 tokens, hidden 7168 bf16, 256
-experts, top-8 with Zipf(1.2) popularity, contiguous (normal-mode) layout.
-The low-latency decode workload (8 x 128 tokens, packed masked layout, FP8
-with fp32 scales) is timed alongside and reported under "low_latency".
+The headline workload (`value`) is the normal-mode prefill shape: 8
+simulated ranks x 4096 tokens, hidden 7168 bf16, 256 experts, top-8 with
+Zipf(1.2) popularity, contiguous layout.  The other workloads of the method
+are timed alongside under "workloads": low-latency decode (8 x 128 tokens,
+packed masked, FP8 + fp32 scales), the FP8 training shape (16 x 8192,
+hidden 4096, UE8M0 column-major scales) and the 64-rank message packer.
 
 `value` is algorithmic GB/s: the bytes the method must move (x read once,
 K receive rows written, K rows read back, the output written, plus the
-layout's index traffic) divided by the step time.  Inputs are resident in
-HBM before the timed region.
+layout's index traffic) divided by the step time, with inputs resident in
+HBM before the timed region.  Per-phase times come from HIP events on the
+stream the library launches on (torch's current stream).
 
-Prints one JSON line.  Only one GPU is used: --gpus above 1 exits with a
-message.
+Prints one JSON line.  One GPU only: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
@@ -34,56 +39,54 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+DEFAULT_WORKLOADS = ["normal_prefill", "ll_decode", "fp8_train", "messages"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def layout_bytes(w, send_head=True):
+def layout_bytes(w, rows_written):
+    """topk read, send_pos / is_token_in_rank / send_head written, and one
+    recv_src_idx entry per filled row."""
     R, T, K = w.R, w.T, w.K
     M = R * T * K
-    b = 4 * M            # topk read
-    b += 4 * M           # send_pos written
-    b += R * T * R       # is_token_in_rank written
-    if send_head:
-        b += 4 * R * T * R
+    b = 4 * M + R * T * R + 4 * R * T * R + 4 * rows_written
+    if w.mode != 2:
+        b += 4 * M
     return b
 
 
-def step_bytes(w, rows):
-    """Algorithmic bytes of layout, dispatch and combine for one step."""
+def dispatch_bytes(w):
     R, T, H, K, G = w.R, w.T, w.H, w.K, w.G
     N, M = R * T, R * T * K
-    lay = layout_bytes(w) + 4 * rows  # + recv_src_idx
-    if w.quant == 0:
-        disp = 2 * H * N + 2 * H * M + 4 * M
-    elif w.quant == 1:
-        disp = 2 * H * N + (H + 4 * G) * M + 4 * M
-    else:
-        disp = 2 * H * N + (H + G) * M + 4 * M
-    comb = 2 * H * M + 2 * H * N + 8 * M
-    return lay, disp, comb
+    row = {0: 2 * H, 1: H + 4 * G, 2: H + G}[w.quant]
+    return 2 * H * N + row * M + 4 * M
+
+
+def combine_bytes(w):
+    R, T, H, K = w.R, w.T, w.H, w.K
+    N, M = R * T, R * T * K
+    return 2 * H * M + 2 * H * N + 8 * M
 
 
 def kernel_hash():
     h = hashlib.sha256()
-    for f in ["dispatch.hip", "combine.hip", "quant.hpp", "ep_device.hpp"]:
+    for f in ["dispatch.hip", "combine.hip", "messages.hip", "quant.hpp", "ep_device.hpp"]:
         with open(os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel: str):
+def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/
     counters.json), or None when absent or taken on different kernel code."""
-    path = os.path.join(ROOT, "profiles", "counters.json")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    e = d.get(kernel)
+    e = d.get(f"{workload}:{kernel}")
     if not e or e.get("kernel_hash") != kernel_hash():
         return None
     return e.get("hbm_bytes_per_launch")
@@ -92,14 +95,16 @@ def traffic_from_profile(kernel: str):
 class Runner:
     """Buffers and launches of one workload; everything resident in HBM."""
 
-    def __init__(self, w, torch, ep, inputs):
+    def __init__(self, w, torch, ep, inputs, keep_host=False):
         self.w, self.torch, self.ep = w, torch, ep
         dev = "cuda"
         log(f"[bench] {w.name}: generating inputs")
         topk = inputs.gen_topk(w)
         x = inputs.gen_x(w)
         wt = inputs.gen_weights(w)
-        self.p = ep.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+        self.host = (topk, x, wt) if keep_host else None
+        self.p = ep.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant,
+                            region_bytes=w.region_bytes, epoch=w.epoch)
         self.topk = torch.from_numpy(topk).to(dev)
         self.x = torch.from_numpy(x).view(torch.bfloat16).to(dev)
         self.wt = torch.from_numpy(wt).to(dev)
@@ -107,21 +112,44 @@ class Runner:
         self.ws = ep.workspace(self.p)
         ep.get_layout(self.p, self.topk, self.lay, self.ws)
         torch.cuda.synchronize()
+        self.msgs = self.recv = self.y = self.out = None
+        if w.mode == ep.MODE_MESSAGES:
+            # untimed read-back of the per-pair counts to size the arena
+            send_cap, desc_cap = ep.messages_capacity(self.p, self.lay.num_tokens_per_rank.cpu().numpy())
+            self.msgs = ep.Messages(self.p, send_cap, desc_cap)
+            ep.dispatch(self.p, self.lay, self.x, msgs=self.msgs, topk_idx=self.topk,
+                        topk_weights=self.wt, ws=self.ws)
+            torch.cuda.synchronize()
+            table = self.msgs.table.cpu().numpy()
+            nd = int(self.msgs.num_descriptors.item())
+            msg_bytes = int(table[:, :, 2].sum())
+            lay = layout_bytes(w, 0)
+            disp = 2 * w.H * w.N + 8 * w.K * w.N + msg_bytes + 64 * nd + 64 * w.R * w.R
+            self.bytes = {"layout": lay, "dispatch": disp}
+            self.kernels = {"dispatch": "msg_pack_fp8" if w.quant else "msg_pack_bf16"}
+            self.extra = {"messages": int((table[:, :, 2] > 0).sum()), "descriptors": nd,
+                          "message_bytes": msg_bytes}
+            return
         if w.mode == ep.MODE_NORMAL:
             self.rows = int(self.lay.row_base[-1].item())  # untimed read-back of the receive size
+            filled = self.rows
         else:
             self.rows = w.E * w.R * w.T
+            filled = w.R * w.T * w.K
         self.recv = ep.Recv(self.p, self.rows)
         if w.quant == ep.QUANT_NONE:
             self.y = self.recv.x  # identity expert
         else:
-            # expert outputs in bf16 in the receive layout (values do not
-            # change the data movement)
+            # bf16 expert outputs in the receive layout (values do not change
+            # the data movement)
             self.y = torch.empty((self.rows, w.H), dtype=torch.bfloat16, device=dev)
             self.y.normal_()
         self.out = torch.empty((w.R, w.T, w.H), dtype=torch.bfloat16, device=dev)
-        lb, db, cb = step_bytes(w, self.rows if w.mode == ep.MODE_NORMAL else w.R * w.T * w.K)
-        self.bytes = {"layout": lb, "dispatch": db, "combine": cb}
+        self.bytes = {"layout": layout_bytes(w, filled), "dispatch": dispatch_bytes(w),
+                      "combine": combine_bytes(w)}
+        self.kernels = {"dispatch": "dispatch_copy" if w.quant == 0 else "dispatch_fp8",
+                        "combine": "combine_rows"}
+        self.extra = {}
 
     def step(self, ev=None):
         ep, p = self.ep, self.p
@@ -130,10 +158,15 @@ class Runner:
         ep.get_layout(p, self.topk, self.lay, self.ws)
         if ev is not None:
             ev[1].record()
-        ep.dispatch(p, self.lay, self.x, recv=self.recv, ws=self.ws)
+        if self.msgs is not None:
+            ep.dispatch(p, self.lay, self.x, msgs=self.msgs, topk_idx=self.topk,
+                        topk_weights=self.wt, ws=self.ws)
+        else:
+            ep.dispatch(p, self.lay, self.x, recv=self.recv, ws=self.ws)
         if ev is not None:
             ev[2].record()
-        ep.combine(p, self.lay, self.y, self.wt, self.out)
+        if self.msgs is None:
+            ep.combine(p, self.lay, self.y, self.wt, self.out)
         if ev is not None:
             ev[3].record()
 
@@ -152,14 +185,43 @@ class Runner:
         err = int(self.lay.err.item())
         if err:
             raise RuntimeError(f"device error word {err}")
-        ph = {"layout": [], "dispatch": [], "combine": []}
-        for e in evs:
-            ph["layout"].append(e[0].elapsed_time(e[1]))
-            ph["dispatch"].append(e[1].elapsed_time(e[2]))
-            ph["combine"].append(e[2].elapsed_time(e[3]))
+        names = ["layout", "dispatch", "combine"][: len(self.bytes)]
+        ph = {k: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k in enumerate(names)}
         ms = (t1 - t0) * 1e3 / steps
         return ms, {k: float(np.mean(v)) for k, v in ph.items()}, \
             {k: float(np.median(v)) for k, v in ph.items()}
+
+    def report(self, steps, warmup):
+        w = self.w
+        log(f"[bench] {w.name}: timing {steps} steps after {warmup} warm-up")
+        ms, mean_ph, med_ph = self.run(steps, warmup)
+        total = sum(self.bytes.values())
+        phases = {k: {"ms_mean": round(mean_ph[k], 4), "ms_median": round(med_ph[k], 4),
+                      "bytes": self.bytes[k],
+                      "GBps": round(self.bytes[k] / (mean_ph[k] * 1e-3) / 1e9, 1)}
+                  for k in mean_ph}
+        dom = max(self.kernels, key=lambda k: mean_ph[k])
+        kname = self.kernels[dom]
+        ach = self.bytes[dom] / (mean_ph[dom] * 1e-3) / 1e9
+        mode = {0: "contiguous", 1: "packed-masked", 2: "messages"}[w.mode]
+        payload = {0: "bf16", 1: "fp8-e4m3 fp32 scales", 2: "fp8-e4m3 ue8m0 scales"}[w.quant]
+        res = {
+            "workload": f"{w.name} R{w.R} T{w.T} H{w.H} E{w.E} K{w.K} "
+                        f"{w.routing}{w.alpha if w.routing == 'zipf' else ''} {mode} {payload}",
+            "ms_per_step": round(ms, 4),
+            "GBps": round(total / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.N / (ms * 1e-3), 1),
+            "bytes_per_step": total,
+            "phases": phases,
+            "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBPS, 4),
+                         "traffic": traffic_from_profile(kname, w.name)},
+        }
+        res.update(self.extra)
+        if total < 256e6:
+            res["cache"] = "warm: the step's data fits in the 256 MB last-level cache"
+        return ms, res
 
 
 def copy_probe(torch, nbytes=4 << 30, reps=10):
@@ -182,16 +244,17 @@ def copy_probe(torch, nbytes=4 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, inputs, tokens_per_rank):
+def cpu_baseline(w, host, tokens_per_rank):
     """The plain C oracle on a bounded sample of the workload: the first
     `tokens_per_rank` tokens of every rank, layout + dispatch + combine,
     single-threaded, outputs preallocated and touched before timing."""
     from oracle import oracle as orc
 
+    topk, x, wt = host
     T = tokens_per_rank
-    topk = np.ascontiguousarray(inputs.gen_topk(w)[:, :T])
-    x = np.ascontiguousarray(inputs.gen_x(w)[:, :T])
-    wt = np.ascontiguousarray(inputs.gen_weights(w)[:, :T])
+    topk = np.ascontiguousarray(topk[:, :T])
+    x = np.ascontiguousarray(x[:, :T])
+    wt = np.ascontiguousarray(wt[:, :T])
     p = orc.Problem(w.R, T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
     lay = orc.layout(p, topk)
     rows = lay.total_rows
@@ -203,9 +266,8 @@ def cpu_baseline(w, inputs, tokens_per_rank):
     orc.combine(p, recv, wt, lay.send_pos, out=out)
     dt = time.perf_counter() - t0
     sw = w.replace(T=T)
-    lb, db, cb = step_bytes(sw, rows)
-    gbps = (lb + db + cb) / dt / 1e9
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    nbytes = layout_bytes(sw, rows) + dispatch_bytes(sw) + combine_bytes(sw)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {T} of {w.T} tokens on each of the {w.R} ranks "
                       f"(layout + dispatch + combine, {dt:.2f} s, single thread)",
             "tokens_per_s": round(w.R * T / dt, 1)}
@@ -216,8 +278,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="normal_prefill")
-    ap.add_argument("--no-ll", action="store_true", help="skip the low-latency workload")
+    ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS),
+                    help="comma-separated; the first is the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--calib", action="store_true",
@@ -233,37 +295,23 @@ def main():
     from combine_ep_get_layout_amd import ep, inputs
 
     ep.lib()  # fail loudly if the HIP library is missing
-    w = inputs.WORKLOADS[args.workload]
-    r = Runner(w, torch, ep, inputs)
-    log(f"[bench] {w.name}: timing {args.steps} steps after {args.warmup} warm-up")
-    ms, mean_ph, med_ph = r.run(args.steps, args.warmup)
-    total = sum(r.bytes.values())
-    gbps = total / (ms * 1e-3) / 1e9
-    tok_s = w.N / (ms * 1e-3)
-    dom = max(("dispatch", "combine"), key=lambda k: mean_ph[k])
-    kname = {"dispatch": "dispatch_copy", "combine": "combine_rows"}[dom]
-    ach = r.bytes[dom] / (mean_ph[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(kname)
-    phases = {k: {"ms_mean": round(mean_ph[k], 4), "ms_median": round(med_ph[k], 4),
-                  "bytes": r.bytes[k],
-                  "GBps": round(r.bytes[k] / (mean_ph[k] * 1e-3) / 1e9, 1)} for k in mean_ph}
-    del r
-    torch.cuda.empty_cache()
-
-    ll = None
-    if not args.no_ll and args.workload != "ll_decode":
-        wl = inputs.WORKLOADS["ll_decode"]
-        rl = Runner(wl, torch, ep, inputs)
-        ms_l, mean_l, _ = rl.run(max(args.steps, 20), args.warmup)
-        tb = sum(rl.bytes.values())
-        ll = {"workload": "ll_decode R8 T128 H7168 E256 K8 uniform, packed masked, fp8 e4m3 fp32 scales",
-              "ms_per_step": round(ms_l, 4), "GBps": round(tb / (ms_l * 1e-3) / 1e9, 1),
-              "tokens_per_s": round(wl.N / (ms_l * 1e-3), 1), "bytes_per_step": tb,
-              "phase_ms": {k: round(v, 4) for k, v in mean_l.items()},
-              "cache": "warm: the step's data fits in the 256 MB last-level cache"}
-        del rl
+    names = [n for n in args.workloads.split(",") if n]
+    head = None
+    others = {}
+    cpu = None
+    for i, name in enumerate(names):
+        w = inputs.WORKLOADS[name]
+        r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu))
+        steps = args.steps if i == 0 else max(5, min(args.steps, 20))
+        ms, res = r.report(steps, args.warmup)
+        if i == 0:
+            head = (w, ms, res)
+            if not args.no_cpu:
+                host = r.host
+        else:
+            others[name] = res
+        del r
         torch.cuda.empty_cache()
-
     if args.calib:
         a = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
         b = torch.empty_like(a)
@@ -272,33 +320,32 @@ def main():
         torch.cuda.synchronize()
         del a, b
     probe = copy_probe(torch)
-    cpu = None if args.no_cpu else cpu_baseline(w, inputs, args.cpu_tokens)
+    w, ms, res = head
+    if not args.no_cpu and w.mode != ep.MODE_MESSAGES:
+        cpu = cpu_baseline(w, host, min(args.cpu_tokens, w.T))
 
+    quant_dtype = {0: "bf16", 1: "fp8-e4m3+bf16", 2: "fp8-e4m3+bf16"}[w.quant]
     line = {
         "metric": "dispatch+combine achieved HBM GB/s and tokens/s at 1 GPU (LL and normal)",
-        "value": round(gbps, 1),
+        "value": res["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.quant == 0 else "fp8-e4m3+bf16",
+        "dtype": quant_dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name} R{w.R} T{w.T} H{w.H} E{w.E} K{w.K} "
-                               f"{w.routing}{w.alpha if w.routing == 'zipf' else ''} "
-                               f"{'contiguous' if w.mode == 0 else 'packed-masked'}",
-                   "ranks": w.R, "tokens_per_rank": w.T, "hidden": w.H, "experts": w.E,
-                   "topk": w.K, "bytes_per_step": total},
-        "tokens_per_s": round(tok_s, 1),
-        "phases": phases,
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1),
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic},
+        "config": {"workload": res["workload"], "ranks": w.R, "tokens_per_rank": w.T,
+                   "hidden": w.H, "experts": w.E, "topk": w.K,
+                   "bytes_per_step": res["bytes_per_step"]},
+        "tokens_per_s": res["tokens_per_s"],
+        "phases": res["phases"],
+        "roofline": res["roofline"],
         "copy_probe_GBps": round(probe, 1),
-        "low_latency": ll,
+        "workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

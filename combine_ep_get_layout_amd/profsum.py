@@ -56,6 +56,7 @@ def main():
     ap.add_argument("--json")
     ap.add_argument("--cmd", required=True, help="the bench command that was profiled")
     ap.add_argument("--title", default="bench.py")
+    ap.add_argument("--workload", required=True, help="workload name the runs measured")
     args = ap.parse_args()
 
     ks = kernel_stats(args.trace)
@@ -101,10 +102,12 @@ def main():
         if os.path.exists(args.json):
             d = json.load(open(args.json))
         for k, v in traffic.items():
-            for short in ("dispatch_copy", "combine_rows", "dispatch_fp8", "msg_pack_fp8"):
+            for short in ("dispatch_copy", "combine_rows", "dispatch_fp8", "msg_pack_fp8",
+                          "msg_pack_bf16"):
                 if short in k:
-                    d[short] = {"hbm_bytes_per_launch": round(v), "kernel": k,
-                                "kernel_hash": kernel_hash(), "workload": args.title}
+                    d[f"{args.workload}:{short}"] = {"hbm_bytes_per_launch": round(v), "kernel": k,
+                                                     "kernel_hash": kernel_hash(),
+                                                     "title": args.title}
         json.dump(d, open(args.json, "w"), indent=1)
     print("\n".join(lines))
 
