@@ -94,13 +94,13 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
     }
     u32x4* dst = codes + (int64_t)row * P;
     int64_t sbase, sstride;
-    if (LL) {
+    if (LL) {  // column-major per expert, written in place
       const int e = row / RT, pos = row - e * RT;
       sbase = (int64_t)e * G * RT + pos;
       sstride = RT;
-    } else {
-      sbase = row;
-      sstride = cap;
+    } else {  // row-major staging; scales_to_columns transposes it
+      sbase = (int64_t)row * G;
+      sstride = 1;
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -119,6 +119,65 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
   }
 }
 
+// Normal-mode FP8 scales: the dispatch kernel stores each row's G scales
+// contiguously in a staging buffer (row-major, coalesced); this kernel
+// writes them column-major, scales[g * cap + row], a tile of consecutive
+// rows per group per store, through LDS.  Rows past the filled part of their
+// expert segment (alignment padding) are not written.  A scattered
+// per-row store of one byte per group would cost a memory transaction per
+// byte instead.
+template <int SB>
+__global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restrict__ stage,
+                                                         uint8_t* __restrict__ scales, int G,
+                                                         int64_t cap, int64_t limit,
+                                                         const int32_t* row_base_end,
+                                                         const int32_t* __restrict__ expert_start,
+                                                         const int32_t* __restrict__ count,
+                                                         int E, int tile_rows) {
+  extern __shared__ uint32_t lds[];
+  int* starts = (int*)lds;                  // E + 1
+  int* filled = starts + E + 1;             // tile_rows
+  uint32_t* tile = (uint32_t*)(filled + tile_rows);  // tile_rows * G * SB bytes
+  const int64_t total = min((int64_t)*row_base_end, limit);  // rows that were staged
+  const int64_t r0 = (int64_t)blockIdx.x * tile_rows;
+  if (r0 >= total) return;
+  const int nrows = (int)min((int64_t)tile_rows, total - r0);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) starts[e] = expert_start[e];
+  if (threadIdx.x == 0) starts[E] = (int)total;
+  const int nbytes = nrows * G * SB;
+  const uint8_t* src = stage + r0 * G * SB;
+  uint8_t* t8 = (uint8_t*)tile;
+  if (SB == 4) {
+    for (int i = threadIdx.x; i < nbytes / 4; i += blockDim.x) tile[i] = ((const uint32_t*)src)[i];
+  } else {
+    for (int i = threadIdx.x; i < nbytes; i += blockDim.x) t8[i] = src[i];
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < tile_rows; r += blockDim.x) {
+    const int64_t row = r0 + r;
+    int ok = 0;
+    if (r < nrows) {
+      int lo = 0, hi = E;  // last e with starts[e] <= row
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (starts[mid] <= row) lo = mid;
+        else hi = mid;
+      }
+      ok = row - starts[lo] < count[lo];
+    }
+    filled[r] = ok;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < G * tile_rows; it += blockDim.x) {
+    const int g = it / tile_rows, r = it % tile_rows;
+    if (r < nrows && filled[r]) {
+      const int64_t di = (int64_t)g * cap + r0 + r;
+      if (SB == 4) ((uint32_t*)scales)[di] = tile[r * G + g];
+      else scales[di] = t8[r * G + g];
+    }
+  }
+}
+
 template <int NV>
 static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
@@ -129,9 +188,31 @@ static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t 
 template <int NP, int Q, bool LL>
 static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
+  // normal mode: rows also index the staging buffer, so they stay below both
+  const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
   hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL>), dim3(N), dim3(kWave * waves), 0, st,
-                     (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, a.recv_scales, P, a.g.K,
-                     a.cap, a.g.G, a.g.R * a.g.T, a.err);
+                     (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
+                     LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, a.err);
+  if (!LL) {
+    // 64 rows per tile, fewer for wide rows (the tile lives in LDS)
+    const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;
+    int tile_rows = 64;
+    while (tile_rows > 8 && (size_t)tile_rows * a.g.G * sb > 32768) tile_rows >>= 1;
+    const size_t lds = sizeof(int) * (a.g.E + 1 + tile_rows) + (size_t)tile_rows * a.g.G * sb + 16;
+    const int64_t tiles = (cap + tile_rows - 1) / tile_rows;
+    if (tiles > 0) {
+      if (Q == EP_QUANT_FP8_F32)
+        hipLaunchKernelGGL(scales_to_columns<4>, dim3((unsigned)tiles), dim3(256), lds, st,
+                           (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
+                           a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
+                           tile_rows);
+      else
+        hipLaunchKernelGGL(scales_to_columns<1>, dim3((unsigned)tiles), dim3(256), lds, st,
+                           (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
+                           a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
+                           tile_rows);
+    }
+  }
 }
 
 template <int Q, bool LL>

@@ -89,6 +89,12 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   off += up256(sizeof(int32_t) * (size_t)R * T * R);
   g->off_msg = off;
   if (p->mode == EP_MODE_MESSAGES) off += up256(message_ws_bytes(R));
+  g->off_stage = off;
+  if (p->mode == EP_MODE_NORMAL && p->quant != EP_QUANT_NONE) {
+    // row-major scale staging for the worst-case number of receive rows
+    const int64_t rows = entries + (int64_t)E * (p->expert_alignment - 1);
+    off += up256((size_t)rows * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
+  }
   g->ws_bytes = off < 256 ? 256 : off;
   return EP_OK;
 }
@@ -192,10 +198,23 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
     if (recv->capacity < 0) return EP_ERR_CAPACITY;
     if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
       return EP_ERR_CAPACITY;
+    const bool staged = p->mode == EP_MODE_NORMAL && p->quant != EP_QUANT_NONE;
+    if (staged && toks) {
+      if (!workspace || !layout->expert_start || !layout->recv_tokens_per_expert ||
+          !layout->row_base)
+        return EP_ERR_NULL;
+      if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
+      if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
+    }
     ep::DispatchArgs a;
     a.g = g;
     a.mode = p->mode;
     a.quant = p->quant;
+    a.stage = staged ? (char*)workspace + g.off_stage : nullptr;
+    a.stage_rows = (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+    a.expert_start = layout->expert_start;
+    a.recv_per_expert = layout->recv_tokens_per_expert;
+    a.row_base = layout->row_base;
     a.x = x;
     a.send_pos = layout->send_pos;
     a.recv_x = recv->x;

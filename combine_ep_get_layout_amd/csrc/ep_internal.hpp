@@ -23,7 +23,7 @@ struct Geometry {
   int ebits;   // bits of an expert id
   int rbits;   // bits of a rank id
   // workspace carve-up (byte offsets from the workspace base)
-  size_t off_hist_e, off_hist_r, off_local_e, off_local_r, off_msg, ws_bytes;
+  size_t off_hist_e, off_hist_r, off_local_e, off_local_r, off_msg, off_stage, ws_bytes;
 };
 
 int make_geometry(const ep_problem* p, Geometry* g);  // EP_OK or EP_ERR_*
@@ -63,6 +63,13 @@ struct DispatchArgs {
   void* recv_scales;
   int64_t cap;
   int32_t* err;
+  // normal-mode FP8: row-major scale staging (workspace) and the layout's
+  // segment starts / counts / row bases used to transpose it column-major
+  void* stage;
+  int64_t stage_rows;  // rows the staging buffer holds
+  const int32_t* expert_start;
+  const int32_t* recv_per_expert;
+  const int32_t* row_base;
 };
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);

@@ -435,3 +435,34 @@ def test_combine_without_expert_rows_flags_every_entry():
     torch.cuda.synchronize()
     assert int(h(gl.err)[0]) & ep.DEVERR_CAPACITY
     assert (out.float() == 0).all().item()
+
+
+@pytest.mark.parametrize("quant", [QF, QU])
+def test_fp8_normal_capacity_and_scale_canaries(quant):
+    """FP8 normal dispatch into too few rows: error bit, codes and scales of
+    the rows that fit are right, nothing is written past either buffer."""
+    w = inputs.small("fp8cap", R=2, T=48, H=256, E=8, K=3, quant=quant, seed=12)
+    topk = inputs.gen_topk(w)
+    x = inputs.gen_x(w)
+    p, po = problems(w, align=2)
+    ol = orc.layout(po, topk)
+    gl, ws = gpu_layout(p, topk)
+    cap = ol.total_rows - 9
+    recv = ep.Recv(p, cap)
+    big_x = torch.full((cap + 4, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    recv.x = big_x[:cap]
+    dt = torch.float32 if quant == QF else torch.uint8
+    big_s = torch.full((w.G * cap + 64,), 7, dtype=dt, device=DEV)
+    recv.scales = big_s[: w.G * cap]
+    ep.dispatch(p, gl, torch.from_numpy(x).view(torch.bfloat16).to(DEV), recv=recv, ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(gl.err)[0]) & ep.DEVERR_CAPACITY
+    assert (h(big_x[cap:]) == 0xA5).all()
+    assert (h(big_s[w.G * cap:]) == 7).all()
+    _, oc, osc = orc.dispatch(po, x, topk, ol.send_pos, ol.total_rows)
+    rows = ol.send_pos[(ol.send_pos >= 0) & (ol.send_pos < cap)]
+    assert np.array_equal(h(recv.x)[rows], oc[rows])
+    gsc = h(big_s)
+    for r in rows:
+        g = np.arange(w.G)
+        assert np.array_equal(gsc[g * cap + r], osc[g * ol.total_rows + r]), r
