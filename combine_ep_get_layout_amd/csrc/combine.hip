@@ -89,6 +89,7 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
 // each wave keeps a full set of loads in flight while it computes.
 constexpr int kPipeK = 8;
 constexpr int kPipeTokens = 2;
+constexpr int64_t kPipeMinTokens = 8192;
 
 __device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, int K, int j,
                                            int V, int64_t y_rows, u32x4 (&v)[kPipeK]) {
@@ -176,7 +177,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   int nv = 1;
   while ((V + kWave * nv - 1) / (kWave * nv) > 16) ++nv;
   const int waves = (V + kWave * nv - 1) / (kWave * nv);
-  if (nv == 1 && a.g.K <= kPipeK) {
+  // two tokens per block only when there are enough blocks to fill the chip
+  if (nv == 1 && a.g.K <= kPipeK && N >= kPipeMinTokens) {
     const int n = (int)N;
     hipLaunchKernelGGL(combine_rows_pipe, dim3((n + kPipeTokens - 1) / kPipeTokens),
                        dim3(kWave * waves), 0, st, (const u32x4*)a.y, a.send_pos, a.w,

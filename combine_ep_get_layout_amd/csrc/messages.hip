@@ -9,17 +9,18 @@
 // the Bone", WQE anatomy (16-byte segments in a 64-byte block) and Ordering
 // (payload stores visible before the store that announces them).
 //
-// Three launches:
-//   1. table  : one block.  Region size per (source, destination) from the
-//               token counts; compact offsets in each source's send arena
-//               (prefix over destinations) and each destination's receive
-//               arena (prefix over sources); arena bases rounded to the region
-//               size; descriptor counts and their prefix.
-//   2. pack   : one wavefront per token row piece.  The row is read once and
+// Four launches:
+//   1. offsets: one block per source (region sizes from the token counts,
+//               compact offsets in its send arena: prefix over destinations)
+//               and one per destination (offsets in its receive arena: prefix
+//               over sources; descriptor count of each message).
+//   2. rows   : one block per source: arena bases rounded to the region size,
+//               first descriptor of each message, the table row.
+//   3. pack   : one wavefront per token row piece.  The row is read once and
 //               quantised once, then stored into every message that carries
 //               the token, at index send_head[s][t][d] within the message,
 //               with the token's scales, weights, expert ids and index.
-//   3. finish : one thread per message: section padding, header, then (after
+//   4. finish : one thread per message: section padding, header, then (after
 //               a fence) the completion flag, then the descriptors.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
@@ -71,10 +72,12 @@ __device__ inline int64_t count_chunks(int64_t la, int64_t ra, int64_t len, int6
 }
 
 struct MsgWs {
-  int64_t* region;   // [R*R]
-  int64_t* send_loc; // [R*R] offset within the source's arena
-  int64_t* recv_loc; // [R*R] offset within the destination's arena
-  int64_t* dcount;   // [R*R]
+  int64_t* region;    // [R*R] region bytes (0 = no message)
+  int64_t* send_loc;  // [R*R] offset within the source's arena
+  int64_t* recv_loc;  // [R*R] offset within the destination's arena
+  int64_t* dcount;    // [R*R] descriptors of the message
+  int64_t* send_tot;  // [R] bytes of each source's messages
+  int64_t* recv_tot;  // [R] bytes of each destination's messages
 };
 
 __device__ inline MsgWs msg_ws(void* ws, int R) {
@@ -85,133 +88,125 @@ __device__ inline MsgWs msg_ws(void* ws, int R) {
   w.send_loc = p + rr;
   w.recv_loc = p + 2 * rr;
   w.dcount = p + 3 * rr;
+  w.send_tot = p + 4 * rr;
+  w.recv_tot = p + 4 * rr + R;
   return w;
 }
 
-// Exclusive scan of a strided sequence of n int64 by one wavefront; returns
-// the total.
-__device__ int64_t wave_scan_strided(const int64_t* in, int64_t* out, int n, int64_t stride) {
-  const int lane = lane_id();
-  int64_t carry = 0;
-  for (int b = 0; b < n; b += kWave) {
-    const int i = b + lane;
-    const int64_t v = i < n ? in[i * stride] : 0;
-    int64_t incl = v;
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int64_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    if (i < n) out[i * stride] = carry + incl - v;
-    carry += __shfl(incl, kWave - 1);
-  }
-  return carry;
+__device__ __forceinline__ int64_t region_of(int64_t n, int H, int K, int quant) {
+  return n > 0 ? 32 + msg_sections(n, H, K, quant).body : 0;
 }
 
-__global__ __launch_bounds__(1024) void msg_table(MessageArgs a) {
+// Exclusive scan of one int64 per thread over the block; *total = sum.
+__device__ int64_t block_scan64(int64_t v, int64_t* total) {
+  __shared__ int64_t wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t incl = v;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) before += wsum[w];
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ int64_t message_descriptors(int64_t reg, int64_t la, int64_t ra,
+                                                       int64_t rb) {
+  if (reg == 0) return 0;
+  const int64_t body = reg - 32;
+  return count_chunks(la + 16, ra + 16, body, rb) + count_chunks(la, ra, 16, rb) +
+         count_chunks(la + 16 + body, ra + 16 + body, 16, rb);
+}
+
+// Blocks [0, R): source s: region sizes of its messages and their offsets
+// in s's arena (prefix over destinations).  Blocks [R, 2R): destination d:
+// offsets in d's arena (prefix over sources) and the descriptor count of
+// every message to d (its send offset re-derived from s's row).
+// One thread per rank (R <= 256 = blockDim).
+__global__ __launch_bounds__(256) void msg_offsets(MessageArgs a) {
   const Geometry& g = a.g;
   const int R = g.R;
-  const int rr = R * R;
   MsgWs w = msg_ws(a.ws, R);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
-  __shared__ int64_t tot_send[257], tot_recv[257];
+  const int i = threadIdx.x;
+  if ((int)blockIdx.x < R) {
+    const int s = blockIdx.x;
+    const int64_t reg = i < R ? region_of(a.cnt_rank[s * R + i], g.H, g.K, a.quant) : 0;
+    int64_t tot;
+    const int64_t off = block_scan64(reg, &tot);
+    if (i < R) {
+      w.region[s * R + i] = reg;
+      w.send_loc[s * R + i] = off;
+    }
+    if (i == 0) w.send_tot[s] = tot;
+  } else {
+    const int d = blockIdx.x - R;
+    const int64_t reg = i < R ? region_of(a.cnt_rank[i * R + d], g.H, g.K, a.quant) : 0;
+    int64_t tot;
+    const int64_t roff = block_scan64(reg, &tot);
+    if (i < R) {
+      w.recv_loc[i * R + d] = roff;
+      int64_t soff = 0;  // offset of (i, d) in source i's arena
+      for (int d2 = 0; d2 < d; ++d2) soff += region_of(a.cnt_rank[i * R + d2], g.H, g.K, a.quant);
+      w.dcount[i * R + d] = message_descriptors(reg, soff, roff, a.region_bytes);
+    }
+    if (i == 0) w.recv_tot[d] = tot;
+  }
+}
 
-  for (int i = tid; i < rr; i += blockDim.x) {
-    const int64_t n = a.cnt_rank[i];
-    w.region[i] = n > 0 ? 32 + msg_sections(n, g.H, g.K, a.quant).body : 0;
-  }
+// Block s: arena bases (every block re-derives them), the first descriptor
+// of each of s's messages (descriptors of all earlier sources, then a
+// prefix over destinations) and s's table row.
+__global__ __launch_bounds__(256) void msg_rows(MessageArgs a) {
+  __shared__ int64_t base_s[257], base_r[257];
+  const Geometry& g = a.g;
+  const int R = g.R;
+  MsgWs w = msg_ws(a.ws, R);
+  const int s = blockIdx.x, i = threadIdx.x;
+  const int64_t rb = a.region_bytes;
+  int64_t tot;
+  const int64_t vs = i < R ? (w.send_tot[i] + rb - 1) / rb * rb : 0;
+  const int64_t os = block_scan64(vs, &tot);
+  if (i < R) base_s[i] = os;
+  if (i == 0) base_s[R] = tot;
+  const int64_t vr = i < R ? (w.recv_tot[i] + rb - 1) / rb * rb : 0;
+  const int64_t orr = block_scan64(vr, &tot);
+  if (i < R) base_r[i] = orr;
+  if (i == 0) base_r[R] = tot;
   __syncthreads();
-  // send side: per source, prefix over destinations; receive side: per
-  // destination, prefix over sources
-  for (int s = wave; s < R; s += nw) {
-    const int64_t t = wave_scan_strided(w.region + (int64_t)s * R, w.send_loc + (int64_t)s * R, R, 1);
-    if (lane == 0) tot_send[s] = t;
-  }
-  for (int d = wave; d < R; d += nw) {
-    const int64_t t = wave_scan_strided(w.region + d, w.recv_loc + d, R, R);
-    if (lane == 0) tot_recv[d] = t;
-  }
-  __syncthreads();
-  // arena bases (each rank's arena starts on a region boundary)
-  if (wave == 0) {
-    const int64_t rb = a.region_bytes;
-    int64_t cs = 0, cr = 0;
-    for (int b = 0; b < R; b += kWave) {
-      const int i = b + lane;
-      int64_t vs = i < R ? (tot_send[i] + rb - 1) / rb * rb : 0;
-      int64_t vr = i < R ? (tot_recv[i] + rb - 1) / rb * rb : 0;
-      int64_t is = vs, ir = vr;
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int64_t ts = __shfl_up(is, o), tr = __shfl_up(ir, o);
-        if (lane >= o) {
-          is += ts;
-          ir += tr;
-        }
-      }
-      if (i < R) {
-        a.arena_base[i] = cs + is - vs;
-        a.arena_base[R + 1 + i] = cr + ir - vr;
-      }
-      cs += __shfl(is, kWave - 1);
-      cr += __shfl(ir, kWave - 1);
+  if (s == 0)
+    for (int j = i; j <= R; j += blockDim.x) {
+      a.arena_base[j] = base_s[j];
+      a.arena_base[R + 1 + j] = base_r[j];
     }
-    if (lane == 0) {
-      a.arena_base[R] = cs;
-      a.arena_base[2 * R + 1] = cr;
-    }
-  }
-  // descriptor counts
-  for (int i = tid; i < rr; i += blockDim.x) {
-    const int64_t reg = w.region[i];
-    int64_t c = 0;
-    if (reg > 0) {
-      const int64_t body = reg - 32, la = w.send_loc[i], ra = w.recv_loc[i];
-      c = count_chunks(la + 16, ra + 16, body, a.region_bytes) + count_chunks(la, ra, 16, a.region_bytes) +
-          count_chunks(la + 16 + body, ra + 16 + body, 16, a.region_bytes);
-    }
-    w.dcount[i] = c;
-  }
-  __syncthreads();
-  // prefix of descriptor counts in (s, d) order: per-thread runs + block scan
-  __shared__ int64_t part[1024];
-  const int per = (rr + blockDim.x - 1) / blockDim.x;
-  const int lo = min(rr, tid * per), hi = min(rr, lo + per);
-  int64_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += w.dcount[i];
-  part[tid] = sum;
-  __syncthreads();
-  if (wave == 0) {
-    // scan of the 1024 partial sums by one wavefront (16 per lane)
-    const int per_lane = blockDim.x / kWave;
-    int64_t loc = 0;
-    for (int q = 0; q < per_lane; ++q) loc += part[lane * per_lane + q];
-    int64_t incl = loc;
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int64_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    int64_t run = incl - loc;
-    for (int q = 0; q < per_lane; ++q) {
-      const int64_t v = part[lane * per_lane + q];
-      part[lane * per_lane + q] = run;
-      run += v;
-    }
-    if (lane == kWave - 1) *a.num_desc = incl;
-  }
-  __syncthreads();
-  int64_t run = part[tid];
-  for (int i = lo; i < hi; ++i) {
-    const int s = i / R, d = i % R;
-    int64_t* row = a.table + (int64_t)i * 8;
-    const int64_t reg = w.region[i];
-    row[0] = reg > 0 ? a.arena_base[s] + w.send_loc[i] : -1;
-    row[1] = reg > 0 ? a.arena_base[R + 1 + d] + w.recv_loc[i] : -1;
+  // descriptors of sources before s
+  int64_t part = 0;
+  for (int64_t j = i; j < (int64_t)s * R; j += blockDim.x) part += w.dcount[j];
+  int64_t before;
+  block_scan64(part, &before);
+  const int64_t dc = i < R ? w.dcount[s * R + i] : 0;
+  int64_t row_total;
+  const int64_t first = before + block_scan64(dc, &row_total);
+  if (s == R - 1 && i == 0) *a.num_desc = before + row_total;
+  if (i < R) {
+    const int64_t sd = (int64_t)s * R + i;
+    const int64_t reg = w.region[sd];
+    int64_t* row = a.table + sd * 8;
+    row[0] = reg > 0 ? base_s[s] + w.send_loc[sd] : -1;
+    row[1] = reg > 0 ? base_r[i] + w.recv_loc[sd] : -1;
     row[2] = reg;
-    row[3] = a.cnt_rank[i];
+    row[3] = a.cnt_rank[sd];
     row[4] = reg > 0 ? reg - 32 : 0;
-    row[5] = run;
-    row[6] = w.dcount[i];
+    row[5] = first;
+    row[6] = dc;
     row[7] = 0;
-    run += w.dcount[i];
   }
 }
 
@@ -226,25 +221,38 @@ __device__ __forceinline__ void store_token_meta(uint8_t* body, const MsgSection
   if (lane == 0) ((int32_t*)(body + m.off[4]))[j] = t;
 }
 
-// Destinations of token (s, t): walk send_head in slabs of 64 ranks; for
-// each destination d the token goes to, call f(d, j) with j its index in
-// the (s, d) message (uniform across the wave).
+// Destinations of token (s, t): walk send_head in slabs of 64 ranks, each
+// lane loading one destination's slot, message offset and token count, so
+// the loop below reads them with readlane instead of a load per message.
+// For each destination d the token goes to, call f(d, j, off, n) with j its
+// index in the (s, d) message, off the message's send offset and n its
+// token count (uniform across the wave).
 template <typename F>
-__device__ __forceinline__ void for_each_destination(const int32_t* head_row, int R, F&& f) {
+__device__ __forceinline__ void for_each_destination(const int32_t* head_row,
+                                                     const int64_t* table_row,
+                                                     const int32_t* cnt_row, int R, F&& f) {
   const int lane = lane_id();
   for (int slab = 0; slab < R; slab += kWave) {
     const int d = slab + lane;
     const int h = d < R ? head_row[d] : -1;
+    int64_t off = -1;
+    int n = 0;
+    if (h >= 0) {
+      off = table_row[(int64_t)d * 8];
+      n = cnt_row[d];
+    }
     uint64_t mask = __ballot(h >= 0);
     while (mask) {
       const int b = __builtin_ctzll(mask);
       mask &= mask - 1;
-      f(slab + b, __builtin_amdgcn_readlane(h, b));
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)off, b);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)off >> 32), b);
+      f(slab + b, __builtin_amdgcn_readlane(h, b), (int64_t)(((uint64_t)hi << 32) | lo),
+        (int64_t)__builtin_amdgcn_readlane(n, b));
     }
   }
 }
 
-// Grid: x = token / 4 (one wavefront per token, tok = s * T + t), y = piece.
 template <int NP, int Q>
 __global__ __launch_bounds__(256) void msg_pack_fp8(MessageArgs a, int P) {
   const Geometry& g = a.g;
@@ -263,10 +271,10 @@ __global__ __launch_bounds__(256) void msg_pack_fp8(MessageArgs a, int P) {
   for (int i = 0; i < NP; ++i) quantise_pair<Q>(lo[i], hi[i], cv[i], scf[i], sce[i]);
   const float* wrow = a.w + (int64_t)tok * g.K;
   const int32_t* idrow = a.topk + (int64_t)tok * g.K;
-  for_each_destination(a.send_head + (int64_t)tok * g.R, g.R, [&](int d, int j) {
-    const int64_t sd = (int64_t)s * g.R + d;
-    const int64_t off = a.table[sd * 8 + 0];
-    const int64_t n = a.cnt_rank[sd];
+  for_each_destination(a.send_head + (int64_t)tok * g.R, a.table + (int64_t)s * g.R * 8,
+                       a.cnt_rank + (int64_t)s * g.R, g.R,
+                       [&](int d, int j, int64_t off, int64_t n) {
+    (void)d;
     const MsgSections m = msg_sections(n, g.H, g.K, Q);
     if (off < 0 || j >= n || off + 32 + m.body > a.arena_cap) {
       if (lane == 0) set_err(a.err, EP_DEVERR_CAPACITY);
@@ -308,10 +316,10 @@ __global__ __launch_bounds__(256) void msg_pack_bf16(MessageArgs a, int V) {
   }
   const float* wrow = a.w + (int64_t)tok * g.K;
   const int32_t* idrow = a.topk + (int64_t)tok * g.K;
-  for_each_destination(a.send_head + (int64_t)tok * g.R, g.R, [&](int d, int j) {
-    const int64_t sd = (int64_t)s * g.R + d;
-    const int64_t off = a.table[sd * 8 + 0];
-    const int64_t n = a.cnt_rank[sd];
+  for_each_destination(a.send_head + (int64_t)tok * g.R, a.table + (int64_t)s * g.R * 8,
+                       a.cnt_rank + (int64_t)s * g.R, g.R,
+                       [&](int d, int j, int64_t off, int64_t n) {
+    (void)d;
     const MsgSections m = msg_sections(n, g.H, g.K, EP_QUANT_NONE);
     if (off < 0 || j >= n || off + 32 + m.body > a.arena_cap) {
       if (lane == 0) set_err(a.err, EP_DEVERR_CAPACITY);
@@ -425,11 +433,12 @@ static void launch_pack_bf16(const MessageArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(msg_pack_bf16<NV>, dim3((N + 3) / 4, npieces), dim3(256), 0, st, a, V);
 }
 
-size_t message_ws_bytes(int R) { return sizeof(int64_t) * 4 * (size_t)R * R; }
+size_t message_ws_bytes(int R) { return sizeof(int64_t) * (4 * (size_t)R * R + 2 * (size_t)R); }
 
 hipError_t launch_messages(const MessageArgs& a, hipStream_t st) {
   const int R = a.g.R;
-  hipLaunchKernelGGL(msg_table, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(msg_offsets, dim3(2 * R), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(msg_rows, dim3(R), dim3(256), 0, st, a);
   if ((int64_t)a.g.R * a.g.T > 0) {
     if (a.quant == EP_QUANT_FP8_F32) {
       launch_pack_q<EP_QUANT_FP8_F32>(a, st);
