@@ -191,8 +191,11 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
   if (!aligned(x, 16) || !aligned(layout->err, 4)) return EP_ERR_ALIGN;
   if (p->mode != EP_MODE_MESSAGES) {
     if (!recv) return EP_ERR_NULL;
-    if (toks && (!recv->x || !layout->send_pos)) return EP_ERR_NULL;
-    if (toks && p->quant != EP_QUANT_NONE && !recv->scales) return EP_ERR_NULL;
+    // receive buffers may be NULL when they have no rows
+    const bool rows = recv->capacity > 0;
+    if (toks && !layout->send_pos) return EP_ERR_NULL;
+    if (toks && rows && !recv->x) return EP_ERR_NULL;
+    if (toks && rows && p->quant != EP_QUANT_NONE && !recv->scales) return EP_ERR_NULL;
     if (!aligned(recv->x, 16) || !aligned(layout->send_pos, 4)) return EP_ERR_ALIGN;
     if (recv->scales && !aligned(recv->scales, 4)) return EP_ERR_ALIGN;
     if (recv->capacity < 0) return EP_ERR_CAPACITY;
@@ -227,10 +230,10 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
     return EP_OK;
   }
   // message mode
-  if (!msgs || !topk_idx || !topk_weights || !layout->send_head || !layout->num_tokens_per_rank ||
-      !msgs->send_arena || !msgs->table || !msgs->arena_base || !msgs->descriptors ||
-      !msgs->num_descriptors || !workspace)
+  if (!msgs || !layout->num_tokens_per_rank || !msgs->send_arena || !msgs->table ||
+      !msgs->arena_base || !msgs->descriptors || !msgs->num_descriptors || !workspace)
     return EP_ERR_NULL;
+  if (toks && (!topk_idx || !topk_weights || !layout->send_head)) return EP_ERR_NULL;
   if (!aligned(msgs->send_arena, 16) || !aligned(msgs->descriptors, 16) ||
       !aligned(msgs->table, 8) || !aligned(msgs->arena_base, 8) ||
       !aligned(msgs->num_descriptors, 8) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
