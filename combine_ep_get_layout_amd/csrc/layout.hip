@@ -28,21 +28,16 @@ namespace ep {
 
 constexpr int kLayoutWaves = 4;  // most wavefronts (chunks) per count block
 
-__global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
-  extern __shared__ int32_t smem[];
+// Count one chunk of source rank s (tokens [t_begin, t_end)) with one
+// wavefront.  cnt_e[E], cnt_r[R] (LDS, zeroed here) end up holding the
+// chunk's histograms; rowbuf[tb*R] is scratch.  Writes each entry's rank
+// in its chunk (local_e) and each token's per-rank stream rank in its
+// chunk (local_r, -1 when not sent), and is_token_in_rank.
+__device__ void count_chunk(const LayoutArgs& a, int s, int t_begin, int t_end, int32_t* cnt_e,
+                            int32_t* cnt_r, int32_t* rowbuf) {
   const Geometry& g = a.g;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int chunk = blockIdx.x * (blockDim.x >> 6) + wave;
-  if (chunk >= g.NC) return;  // uniform per wave
-  const int per_wave = g.E + g.R + g.tb * g.R;
-  int32_t* cnt_e = smem + wave * per_wave;
-  int32_t* cnt_r = cnt_e + g.E;
-  int32_t* rowbuf = cnt_r + g.R;
-  for (int i = lane; i < g.E + g.R; i += kWave) cnt_e[i] = 0;
-
-  const int s = chunk / g.C, c = chunk % g.C;
-  const int t_begin = c * g.ct;
-  const int t_end = min(g.T, t_begin + g.ct);
+  const int lane = lane_id();
+  for (int i = lane; i < g.E + g.R; i += kWave) cnt_e[i] = 0;  // cnt_r follows cnt_e
   const int K = g.K;
   const int my_tok = lane / K, my_k = lane % K;
   const int nent = g.tb * K;
@@ -89,6 +84,21 @@ __global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
       a.local_r[rbase + i] = v;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
+  extern __shared__ int32_t smem[];
+  const Geometry& g = a.g;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (chunk >= g.NC) return;  // uniform per wave
+  const int per_wave = g.E + g.R + g.tb * g.R;
+  int32_t* cnt_e = smem + wave * per_wave;
+  int32_t* cnt_r = cnt_e + g.E;
+  int32_t* rowbuf = cnt_r + g.R;
+  const int s = chunk / g.C, c = chunk % g.C;
+  const int t_begin = c * g.ct;
+  count_chunk(a, s, t_begin, min(g.T, t_begin + g.ct), cnt_e, cnt_r, rowbuf);
   for (int e = lane; e < g.E; e += kWave) a.hist_e[(int64_t)e * g.NC + chunk] = cnt_e[e];
   for (int d = lane; d < g.R; d += kWave) a.hist_r[(int64_t)d * g.NC + chunk] = cnt_r[d];
 }
@@ -203,10 +213,11 @@ __device__ void segment_starts(const LayoutArgs& a, int* start) {
 // Slots: row = segment start + (source, chunk) prefix + rank in chunk, and
 // the token streams' indices.  Block 0 also publishes the segment starts,
 // rows per rank and row bases; padding rows get recv_src_idx = -1.
-__global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
-  __shared__ int start[2049];
+// hist_e / hist_r: the scanned chunk histograms ([E][NC], [R][NC]), in
+// global memory or LDS.
+__device__ void finalize_body(const LayoutArgs& a, const int* start, const int32_t* hist_e,
+                              const int32_t* hist_r) {
   const Geometry& g = a.g;
-  segment_starts(a, start);
   if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e < g.E; e += blockDim.x) a.expert_start[e] = start[e];
     for (int d = threadIdx.x; d <= g.R; d += blockDim.x) {
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
     if (local >= 0) {
       const int64_t st = i / g.K;  // s * T + t
       const int s = (int)(st / g.T), t = (int)(st % g.T);
-      const int pos = a.hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
+      const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
       if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
         set_err(a.err, EP_DEVERR_LL_OVERFLOW);
       } else {
@@ -253,15 +264,88 @@ __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
         const int64_t st = i / g.R;
         const int d = (int)(i % g.R);
         const int s = (int)(st / g.T), t = (int)(st % g.T);
-        v += a.hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
+        v += hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
       }
       a.send_head[i] = v;
     }
   }
 }
 
+__global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
+  __shared__ int start[2049];
+  segment_starts(a, start);
+  finalize_body(a, start, a.hist_e, a.hist_r);
+}
+
+// Small problems: the three phases in one workgroup of 16 wavefronts, one
+// chunk per wavefront (a few per source rank), histograms and scans in LDS,
+// barriers between the phases instead of launches.
+__global__ __launch_bounds__(1024) void layout_fused(LayoutArgs a) {
+  extern __shared__ int32_t smem[];
+  const Geometry& g = a.g;
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per_wave = g.E + g.R + g.tb * g.R;
+  int32_t* hist_e = smem + nw * per_wave;      // [E][NC]
+  int32_t* hist_r = hist_e + g.E * g.NC;       // [R][NC]
+  int* start = hist_r + g.R * g.NC;            // [E + 1]
+  if (threadIdx.x == 0) *a.err = 0;            // errors are raised in phase 3 only
+  // phase 1: chunk histograms and in-chunk ranks
+  int32_t* cnt_e = smem + wave * per_wave;
+  int32_t* cnt_r = cnt_e + g.E;
+  int32_t* rowbuf = cnt_r + g.R;
+  for (int chunk = wave; chunk < g.NC; chunk += nw) {
+    const int s = chunk / g.C, c = chunk % g.C;
+    const int t_begin = c * g.ct;
+    count_chunk(a, s, t_begin, min(g.T, t_begin + g.ct), cnt_e, cnt_r, rowbuf);
+    for (int e = lane; e < g.E; e += kWave) hist_e[e * g.NC + chunk] = cnt_e[e];
+    for (int d = lane; d < g.R; d += kWave) hist_r[d * g.NC + chunk] = cnt_r[d];
+  }
+  __syncthreads();
+  // phase 2: one thread per expert row / destination row of the histograms
+  for (int row = threadIdx.x; row < g.E + g.R; row += blockDim.x) {
+    if (row < g.E) {
+      const int e = row;
+      int run = 0;
+      for (int s = 0; s < g.R; ++s) {
+        const int src0 = run;
+        for (int c = 0; c < g.C; ++c) {
+          const int v = hist_e[e * g.NC + s * g.C + c];
+          hist_e[e * g.NC + s * g.C + c] = run;
+          run += v;
+        }
+        a.cnt_expert[(int64_t)s * g.E + e] = run - src0;
+      }
+      a.recv_per_expert[e] = run;
+    } else {
+      const int d = row - g.E;
+      int acc = 0;
+      for (int s = 0; s < g.R; ++s) {
+        int run = 0;
+        for (int c = 0; c < g.C; ++c) {
+          const int v = hist_r[d * g.NC + s * g.C + c];
+          hist_r[d * g.NC + s * g.C + c] = run;
+          run += v;
+        }
+        a.cnt_rank[s * g.R + d] = run;
+        acc += run;
+        a.rpm[s * g.R + d] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  // phase 3: segment starts, slots
+  segment_starts(a, start);
+  finalize_body(a, start, hist_e, hist_r);
+}
+
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   const Geometry& g = a.g;
+  if (g.fused) {
+    const size_t lds = sizeof(int32_t) * ((size_t)16 * (g.E + g.R + g.tb * g.R) +
+                                          (size_t)(g.E + g.R) * g.NC + g.E + 1);
+    hipLaunchKernelGGL(layout_fused, dim3(1), dim3(1024), lds, stream, a);
+    return hipGetLastError();
+  }
   // LDS per wavefront: expert and rank counters plus one batch of rows;
   // at most 64 KiB per block
   const size_t per_wave = sizeof(int32_t) * (size_t)(g.E + g.R + g.tb * g.R);

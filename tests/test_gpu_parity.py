@@ -29,6 +29,8 @@ SMALL = [
     ("tiny", 2, 8, 128, 8, 2, 1, N, QN, 0.0, 0.0, 0),
     ("ragged", 3, 1000, 256, 12, 3, 4, N, QN, 0.1, 0.1, 0),
     ("k1", 4, 2500, 128, 8, 1, 1, N, QN, 0.05, 0.0, 0),
+    ("multi_launch", 4, 1300, 128, 16, 4, 2, N, QN, 0.05, 0.05, 0),  # > 16384 entries
+    ("multi_launch_ll", 4, 1100, 128, 8, 4, 1, LL, QF, 0.05, 0.0, 0),
     ("k16", 2, 100, 256, 64, 16, 2, N, QN, 0.1, 0.2, 0),
     ("r64", 64, 40, 128, 256, 8, 1, N, QN, 0.0, 0.0, 0),
     ("e_eq_r", 8, 300, 128, 8, 4, 1, N, QN, 0.0, 0.5, 0),
