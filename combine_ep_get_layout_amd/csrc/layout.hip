@@ -26,7 +26,8 @@
 
 namespace ep {
 
-constexpr int kLayoutWaves = 4;  // most wavefronts (chunks) per count block
+constexpr int kLayoutWaves = 4;       // most wavefronts (chunks) per count block
+constexpr int kPrefetchBatches = 16;  // batches whose expert ids are loaded together
 
 // Count one chunk of source rank s (tokens [t_begin, t_end)) with one
 // wavefront.  cnt_e[E], cnt_r[R] (LDS, zeroed here) end up holding the
@@ -45,43 +46,57 @@ __device__ void count_chunk(const LayoutArgs& a, int s, int t_begin, int t_end, 
   const int first_lane = my_tok * K;
   const uint64_t below = lanes_below();
   const uint64_t own_below = below & ~(first_lane == 0 ? 0ull : (~0ull >> (64 - first_lane)));
+  const int nb = (t_end - t_begin + g.tb - 1) / g.tb;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += g.tb) {
-    const int t = t0 + my_tok;
-    const bool in_batch = lane < nent && t < t_end;
-    const int64_t ent = ((int64_t)s * g.T + t) * K + my_k;
-    int e = -1;
-    if (in_batch) e = a.topk[ent];
-    const bool valid = in_batch && e >= 0 && e < g.E;
-    const uint64_t vmask = __ballot(valid);
-
-    // expert level: rank among same-expert entries of this chunk
-    const uint64_t eq = match_key(valid ? (uint32_t)e : 0u, g.ebits, vmask);
-    int slot = -1;
-    if (valid) {
-      slot = cnt_e[e] + rank_below(eq);
-      if ((eq & below) == 0) cnt_e[e] = slot + (int)__popcll(eq);
+  // the expert ids of up to kPrefetchBatches batches are loaded together,
+  // so the chunk pays one memory latency per group instead of one per batch
+  for (int b0 = 0; b0 < nb; b0 += kPrefetchBatches) {
+    int pre[kPrefetchBatches];
+#pragma unroll
+    for (int q = 0; q < kPrefetchBatches; ++q) {
+      const int t = t_begin + (b0 + q) * g.tb + my_tok;
+      const bool in_batch = b0 + q < nb && lane < nent && t < t_end;
+      pre[q] = in_batch ? a.topk[((int64_t)s * g.T + t) * K + my_k] : -1;
     }
-    if (in_batch) a.local_e[ent] = slot;
+#pragma unroll
+    for (int q = 0; q < kPrefetchBatches; ++q) {
+      if (b0 + q >= nb) break;
+      const int t0 = t_begin + (b0 + q) * g.tb;
+      const int t = t0 + my_tok;
+      const bool in_batch = lane < nent && t < t_end;
+      const int64_t ent = ((int64_t)s * g.T + t) * K + my_k;
+      const int e = pre[q];
+      const bool valid = in_batch && e >= 0 && e < g.E;
+      const uint64_t vmask = __ballot(valid);
 
-    // rank level: first entry of a token on each rank, and that token's
-    // rank among the chunk's tokens sent to the rank
-    const int r = valid ? e / g.L : 0;
-    const uint64_t eqr = match_key((uint32_t)r, g.rbits, vmask);
-    const bool first = valid && (eqr & own_below) == 0;
-    const uint64_t eqf = eqr & __ballot(first);
-    for (int i = lane; i < g.tb * g.R; i += kWave) rowbuf[i] = -1;
-    if (first) {
-      const int h = cnt_r[r] + rank_below(eqf);
-      rowbuf[my_tok * g.R + r] = h;
-      if ((eqf & below) == 0) cnt_r[r] = h + (int)__popcll(eqf);
-    }
-    const int nt = min(g.tb, t_end - t0);
-    const int64_t rbase = ((int64_t)s * g.T + t0) * g.R;
-    for (int i = lane; i < nt * g.R; i += kWave) {
-      const int v = rowbuf[i];
-      a.in_rank[rbase + i] = v >= 0 ? 1 : 0;
-      a.local_r[rbase + i] = v;
+      // expert level: rank among same-expert entries of this chunk
+      const uint64_t eq = match_key(valid ? (uint32_t)e : 0u, g.ebits, vmask);
+      int slot = -1;
+      if (valid) {
+        slot = cnt_e[e] + rank_below(eq);
+        if ((eq & below) == 0) cnt_e[e] = slot + (int)__popcll(eq);
+      }
+      if (in_batch) a.local_e[ent] = slot;
+
+      // rank level: first entry of a token on each rank, and that token's
+      // rank among the chunk's tokens sent to the rank
+      const int r = valid ? e / g.L : 0;
+      const uint64_t eqr = match_key((uint32_t)r, g.rbits, vmask);
+      const bool first = valid && (eqr & own_below) == 0;
+      const uint64_t eqf = eqr & __ballot(first);
+      for (int i = lane; i < g.tb * g.R; i += kWave) rowbuf[i] = -1;
+      if (first) {
+        const int h = cnt_r[r] + rank_below(eqf);
+        rowbuf[my_tok * g.R + r] = h;
+        if ((eqf & below) == 0) cnt_r[r] = h + (int)__popcll(eqf);
+      }
+      const int nt = min(g.tb, t_end - t0);
+      const int64_t rbase = ((int64_t)s * g.T + t0) * g.R;
+      for (int i = lane; i < nt * g.R; i += kWave) {
+        const int v = rowbuf[i];
+        a.in_rank[rbase + i] = v >= 0 ? 1 : 0;
+        a.local_r[rbase + i] = v;
+      }
     }
   }
 }
@@ -158,7 +173,7 @@ __device__ void scan_row_segments(int32_t* row, int nseg, int seg, int* seg_star
 // Blocks [E, E+R): destination d's token histogram over (source, chunk):
 // per-source totals (num_tokens_per_rank), the inclusive prefix over
 // sources (rank_prefix_matrix column d), and per-source chunk prefixes.
-__global__ __launch_bounds__(256) void layout_scan(LayoutArgs a) {
+__global__ __launch_bounds__(1024) void layout_scan(LayoutArgs a) {
   __shared__ int seg_start[257];
   const Geometry& g = a.g;
   const int b = blockIdx.x;
@@ -215,8 +230,12 @@ __device__ void segment_starts(const LayoutArgs& a, int* start) {
 // rows per rank and row bases; padding rows get recv_src_idx = -1.
 // hist_e / hist_r: the scanned chunk histograms ([E][NC], [R][NC]), in
 // global memory or LDS.
+struct FirstItems {
+  int e, local, head;
+};
+
 __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32_t* hist_e,
-                              const int32_t* hist_r) {
+                              const int32_t* hist_r, const FirstItems& pre) {
   const Geometry& g = a.g;
   if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e < g.E; e += blockDim.x) a.expert_start[e] = start[e];
@@ -233,33 +252,38 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32
     }
   }
   const int64_t n_ent = (int64_t)g.R * g.T * g.K;
-  const int64_t n_head = (int64_t)g.R * g.T * g.R;
+  const int64_t n_head = a.send_head ? (int64_t)g.R * g.T * g.R : 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int rt = g.R * g.T;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_ent; i += stride) {
-    const int e = a.topk[i];
-    if (e < -1 || e >= g.E) set_err(a.err, EP_DEVERR_TOPK_RANGE);
-    const int local = a.local_e[i];
-    int row = -1;
-    if (local >= 0) {
-      const int64_t st = i / g.K;  // s * T + t
-      const int s = (int)(st / g.T), t = (int)(st % g.T);
-      const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
-      if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
-        set_err(a.err, EP_DEVERR_LL_OVERFLOW);
-      } else {
-        row = start[e] + pos;
-        if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
-          if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
-          else set_err(a.err, EP_DEVERR_CAPACITY);
+  // one index walks both the (token, k) entries and the (token, rank) heads,
+  // so their chunk-prefix gathers are in flight together
+  const int64_t n_all = n_ent > n_head ? n_ent : n_head;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < n_all; i += stride) {
+    const bool is_ent = i < n_ent, is_head = i < n_head;
+    const int e = is_ent ? (i == i0 ? pre.e : a.topk[i]) : 0;
+    const int local = is_ent ? (i == i0 ? pre.local : a.local_e[i]) : -1;
+    int v = is_head ? (i == i0 ? pre.head : a.local_r[i]) : -1;
+    if (is_ent) {
+      if (e < -1 || e >= g.E) set_err(a.err, EP_DEVERR_TOPK_RANGE);
+      int row = -1;
+      if (local >= 0) {
+        const int64_t st = i / g.K;  // s * T + t
+        const int s = (int)(st / g.T), t = (int)(st % g.T);
+        const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
+        if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
+          set_err(a.err, EP_DEVERR_LL_OVERFLOW);
+        } else {
+          row = start[e] + pos;
+          if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
+            if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
+            else set_err(a.err, EP_DEVERR_CAPACITY);
+          }
         }
       }
+      if (a.send_pos) a.send_pos[i] = (a.mode == EP_MODE_MESSAGES) ? -1 : row;
     }
-    if (a.send_pos) a.send_pos[i] = (a.mode == EP_MODE_MESSAGES) ? -1 : row;
-  }
-  if (a.send_head) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_head; i += stride) {
-      int v = a.local_r[i];
+    if (is_head) {
       if (v >= 0) {
         const int64_t st = i / g.R;
         const int d = (int)(i % g.R);
@@ -271,10 +295,25 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32
   }
 }
 
+// A thread's first entry and head, loaded before the segment-start scan so
+// that their memory latency overlaps it.
+__device__ FirstItems first_items(const LayoutArgs& a) {
+  const Geometry& g = a.g;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  FirstItems f{0, -1, -1};
+  if (i0 < (int64_t)g.R * g.T * g.K) {
+    f.e = a.topk[i0];
+    f.local = a.local_e[i0];
+  }
+  if (a.send_head && i0 < (int64_t)g.R * g.T * g.R) f.head = a.local_r[i0];
+  return f;
+}
+
 __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
   __shared__ int start[2049];
+  const FirstItems pre = first_items(a);
   segment_starts(a, start);
-  finalize_body(a, start, a.hist_e, a.hist_r);
+  finalize_body(a, start, a.hist_e, a.hist_r, pre);
 }
 
 // Small problems: the three phases in one workgroup of 16 wavefronts, one
@@ -334,8 +373,9 @@ __global__ __launch_bounds__(1024) void layout_fused(LayoutArgs a) {
   }
   __syncthreads();
   // phase 3: segment starts, slots
+  const FirstItems pre = first_items(a);
   segment_starts(a, start);
-  finalize_body(a, start, hist_e, hist_r);
+  finalize_body(a, start, hist_e, hist_r, pre);
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
@@ -355,7 +395,11 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   const int nb = (g.NC + waves - 1) / waves;
   if (nb > 0)
     hipLaunchKernelGGL(layout_count, dim3(nb), dim3(64 * waves), per_wave * waves, stream, a);
-  hipLaunchKernelGGL(layout_scan, dim3(g.E + g.R), dim3(256), 0, stream, a);
+  // one histogram element per thread where the rows allow
+  int scan_threads = (g.NC + kWave - 1) / kWave * kWave;
+  if (scan_threads < 256) scan_threads = 256;
+  if (scan_threads > 1024) scan_threads = 1024;
+  hipLaunchKernelGGL(layout_scan, dim3(g.E + g.R), dim3(scan_threads), 0, stream, a);
   const int64_t work = (int64_t)g.R * g.T * (g.K > g.R ? g.K : g.R);
   int64_t fb = (work + 255) / 256;
   if (fb > 4096) fb = 4096;
