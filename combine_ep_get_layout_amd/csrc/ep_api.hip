@@ -19,10 +19,10 @@ namespace {
 #define EP_LAYOUT_TARGET_CHUNKS 1024
 #endif
 constexpr int kMaxBatches = 16;  // most batches of entries per layout chunk
-#ifndef EP_FUSED_MAX_ENTRIES
-#define EP_FUSED_MAX_ENTRIES 3072
+#ifndef EP_DIRECT_MAX_ENTRIES
+#define EP_DIRECT_MAX_ENTRIES 6144
 #endif
-constexpr int64_t kFusedMaxEntries = EP_FUSED_MAX_ENTRIES;  // one-workgroup layout up to this many
+constexpr int64_t kDirectMaxEntries = EP_DIRECT_MAX_ENTRIES;  // one-launch layout up to this many
 constexpr int kTargetChunks = EP_LAYOUT_TARGET_CHUNKS;  // wavefronts to spread over the chip
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -72,32 +72,17 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   if (tb > cap) tb = cap;
   if (tb < 1) tb = 1;
   g->tb = tb;
-  // small problems (measured on MI355X: faster than three launches up to
-  // about 3K entries): one chunk per wavefront of a single 16-wave workgroup
-  // (a few chunks per source rank), everything in LDS
-  g->fused = 0;
-  if (entries <= kFusedMaxEntries && T > 0) {
-    const int cps = R >= 16 ? 1 : 16 / R;  // chunks per source
-    const int ct = (T + cps - 1) / cps;
-    const int C = (T + ct - 1) / ct;
-    const int64_t lds_ints = (int64_t)16 * (E + R + tb * R) + (int64_t)(E + R) * R * C + E + 1;
-    if (lds_ints * 4 <= 61440) {  // dynamic LDS, leaving room for the static part
-      g->fused = 1;
-      g->ct = ct;
-      g->C = C;
-      g->NC = R * C;
-    }
-  }
+  // small problems: one launch with a block per expert and per rank, each
+  // reading every entry (16 entries per thread of a 1024-thread block)
+  g->direct = entries <= kDirectMaxEntries ? 1 : 0;
   // fewer, longer chunks only when there are plenty of them
   const int64_t batches = (int64_t)R * ((T + tb - 1) / tb);
   int64_t per = (batches + kTargetChunks - 1) / kTargetChunks;
   if (per < 1) per = 1;
   if (per > kMaxBatches) per = kMaxBatches;
-  if (!g->fused) {
-    g->ct = tb * (int)per;
-    g->C = (T + g->ct - 1) / g->ct;
-    g->NC = R * g->C;
-  }
+  g->ct = tb * (int)per;
+  g->C = (T + g->ct - 1) / g->ct;
+  g->NC = R * g->C;
   g->ebits = bits_for(E);
   g->rbits = bits_for(R);
   size_t off = 0;

@@ -22,7 +22,7 @@ struct Geometry {
   int NC;      // R * C
   int ebits;   // bits of an expert id
   int rbits;   // bits of a rank id
-  int fused;   // small problem: the whole layout in one workgroup
+  int direct;  // small problem: the whole layout in one launch, no chunks
   // workspace carve-up (byte offsets from the workspace base)
   size_t off_hist_e, off_hist_r, off_local_e, off_local_r, off_msg, off_stage, ws_bytes;
 };

@@ -6,7 +6,9 @@
 // recv_src_idx address book), sec. 3.2 (rank of an expert), sec. 4.3
 // (per-expert prefix sums as segment offsets).
 //
-// Three launches, all small next to the data movement they enable:
+// Up to 16K (token, k) entries: one launch (layout_direct, below).  Larger
+// problems take three launches, all small next to the data movement they
+// enable:
 //   1. count   : one wavefront per token chunk.  Entries of a batch (one per
 //                lane, in (token, k) order) find their equal-key peers with
 //                one ballot per key bit; the lowest lane of each key advances
@@ -316,74 +318,258 @@ __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
   finalize_body(a, start, a.hist_e, a.hist_r, pre);
 }
 
-// Small problems: the three phases in one workgroup of 16 wavefronts, one
-// chunk per wavefront (a few per source rank), histograms and scans in LDS,
-// barriers between the phases instead of launches.
-__global__ __launch_bounds__(1024) void layout_fused(LayoutArgs a) {
-  extern __shared__ int32_t smem[];
-  const Geometry& g = a.g;
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int per_wave = g.E + g.R + g.tb * g.R;
-  int32_t* hist_e = smem + nw * per_wave;      // [E][NC]
-  int32_t* hist_r = hist_e + g.E * g.NC;       // [R][NC]
-  int* start = hist_r + g.R * g.NC;            // [E + 1]
-  if (threadIdx.x == 0) *a.err = 0;            // errors are raised in phase 3 only
-  // phase 1: chunk histograms and in-chunk ranks
-  int32_t* cnt_e = smem + wave * per_wave;
-  int32_t* cnt_r = cnt_e + g.E;
-  int32_t* rowbuf = cnt_r + g.R;
-  for (int chunk = wave; chunk < g.NC; chunk += nw) {
-    const int s = chunk / g.C, c = chunk % g.C;
-    const int t_begin = c * g.ct;
-    count_chunk(a, s, t_begin, min(g.T, t_begin + g.ct), cnt_e, cnt_r, rowbuf);
-    for (int e = lane; e < g.E; e += kWave) hist_e[e * g.NC + chunk] = cnt_e[e];
-    for (int d = lane; d < g.R; d += kWave) hist_r[d * g.NC + chunk] = cnt_r[d];
-  }
-  __syncthreads();
-  // phase 2: one thread per expert row / destination row of the histograms
-  for (int row = threadIdx.x; row < g.E + g.R; row += blockDim.x) {
-    if (row < g.E) {
-      const int e = row;
-      int run = 0;
-      for (int s = 0; s < g.R; ++s) {
-        const int src0 = run;
-        for (int c = 0; c < g.C; ++c) {
-          const int v = hist_e[e * g.NC + s * g.C + c];
-          hist_e[e * g.NC + s * g.C + c] = run;
-          run += v;
-        }
-        a.cnt_expert[(int64_t)s * g.E + e] = run - src0;
-      }
-      a.recv_per_expert[e] = run;
-    } else {
-      const int d = row - g.E;
-      int acc = 0;
-      for (int s = 0; s < g.R; ++s) {
-        int run = 0;
-        for (int c = 0; c < g.C; ++c) {
-          const int v = hist_r[d * g.NC + s * g.C + c];
-          hist_r[d * g.NC + s * g.C + c] = run;
-          run += v;
-        }
-        a.cnt_rank[s * g.R + d] = run;
-        acc += run;
-        a.rpm[s * g.R + d] = acc;
-      }
+// Small problems (at most kDirectPer entries per thread of one 1024-thread
+// block): one launch.  Each of the first ceil(E / kDirectExperts) blocks
+// takes kDirectExperts experts and finds the rank of every entry routed to
+// each of them among all such entries in (source, token, k) order, with one
+// block scan over all entries; each of the last R blocks does the same for
+// the tokens sent to one rank.  Every block reads all entries (a few tens of
+// KB, served by the caches), which at this size costs less than chunk
+// histograms and two more launches.  Block 0 also histograms all experts,
+// derives every error condition from the histogram and writes the error
+// word once.
+constexpr int kDirectPer = 16;
+constexpr int kDirectThreads = 1024;
+constexpr int kDirectExperts = 4;
+
+// Exclusive block scan of N ints per thread at once (kDirectThreads
+// threads); total[j] receives the block sums.
+template <int N>
+__device__ void block_exclusive_scan_n(int (&v)[N], int (&total)[N]) {
+  __shared__ int wsum[16][N];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) incl[j] = v[j];
+  for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int n = __shfl_up(incl[j], o);
+      if (lane >= o) incl[j] += n;
     }
   }
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int j = 0; j < N; ++j) wsum[wave][j] = incl[j];
   __syncthreads();
-  // phase 3: segment starts, slots
-  const FirstItems pre = first_items(a);
-  segment_starts(a, start);
-  finalize_body(a, start, hist_e, hist_r, pre);
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    int before = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int x = wsum[w][j];
+      if (w < wave) before += x;
+      all += x;
+    }
+    total[j] = all;
+    v[j] = before + incl[j] - v[j];
+  }
+  __syncthreads();
+}
+
+__device__ void direct_expert_block(const LayoutArgs& a, int e0, int* hist, int* starts,
+                                    int (*src_prefix)[257], int* err_bits) {
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int M = g.R * g.T * g.K, TK = g.T * g.K, rt = g.R * g.T;
+  const bool ll = a.mode == EP_MODE_LOW_LATENCY, msg = a.mode == EP_MODE_MESSAGES;
+  const bool first = e0 == 0;
+  const bool need_hist = first || !ll;
+  const int per = (M + nth - 1) / nth;  // <= kDirectPer
+  const int lo = min(M, tid * per), hi = min(M, lo + per);
+  int ids[kDirectPer];
+#pragma unroll
+  for (int q = 0; q < kDirectPer; ++q) ids[q] = lo + q < hi ? a.topk[lo + q] : -1;
+  if (need_hist)
+    for (int i = tid; i < g.E; i += nth) hist[i] = 0;
+  if (first && tid == 0) *err_bits = 0;
+  __syncthreads();
+  int cnt[kDirectExperts];
+#pragma unroll
+  for (int j = 0; j < kDirectExperts; ++j) cnt[j] = 0;
+  int bad = 0;
+#pragma unroll
+  for (int q = 0; q < kDirectPer; ++q) {
+    if (lo + q >= hi) break;
+    const int id = ids[q];
+#pragma unroll
+    for (int j = 0; j < kDirectExperts; ++j) cnt[j] += id == e0 + j;
+    if (id < -1 || id >= g.E) bad = 1;
+    else if (need_hist && id >= 0) atomicAdd(&hist[id], 1);
+  }
+  if (first && bad) atomicOr(err_bits, EP_DEVERR_TOPK_RANGE);
+  int total[kDirectExperts];
+  block_exclusive_scan_n<kDirectExperts>(cnt, total);  // cnt: prefix; orders the histogram
+  // segment starts: fixed blocks of R*T rows (low-latency), else the
+  // exclusive scan of the counts rounded up to expert_alignment
+  if (!ll) {
+    const int pe = (g.E + nth - 1) / nth;
+    const int elo = min(g.E, tid * pe), ehi = min(g.E, elo + pe);
+    int sum = 0;
+    for (int i = elo; i < ehi; ++i) sum += (hist[i] + a.align - 1) / a.align * a.align;
+    int all;
+    int run = block_exclusive_scan(sum, &all);
+    for (int i = elo; i < ehi; ++i) {
+      starts[i] = run;
+      run += (hist[i] + a.align - 1) / a.align * a.align;
+    }
+    if (tid == 0) starts[g.E] = all;
+    __syncthreads();
+  }
+  int start_e[kDirectExperts];
+#pragma unroll
+  for (int j = 0; j < kDirectExperts; ++j)
+    start_e[j] = e0 + j >= g.E ? 0 : (ll ? (e0 + j) * rt : starts[e0 + j]);
+  // rows of these experts' entries, and the per-source prefixes of their
+  // counts; (source boundary, token, k) tracked incrementally
+  int next_src = TK > 0 ? (lo + TK - 1) / TK : 0;  // first source starting at or after lo
+  int tok = g.K > 0 ? lo / g.K : 0, kk = lo - tok * g.K;
+#pragma unroll
+  for (int q = 0; q < kDirectPer; ++q) {
+    const int i = lo + q;
+    if (i >= hi) break;
+    if (i == next_src * TK) {
+#pragma unroll
+      for (int j = 0; j < kDirectExperts; ++j) src_prefix[j][next_src] = cnt[j];
+      ++next_src;
+    }
+    const int id = ids[q];
+    const int j = id - e0;
+    if (j >= 0 && j < kDirectExperts && id < g.E) {
+      int pos = 0, st = 0;
+#pragma unroll
+      for (int jj = 0; jj < kDirectExperts; ++jj)
+        if (jj == j) {
+          pos = cnt[jj]++;
+          st = start_e[jj];
+        }
+      const int row = ll ? (pos < rt ? st + pos : -1) : st + pos;
+      if (!msg && row >= 0 && a.recv_src_idx && row < a.recv_cap) a.recv_src_idx[row] = tok;
+      if (a.send_pos) a.send_pos[i] = msg ? -1 : row;
+    } else if (first && (id < 0 || id >= g.E) && a.send_pos) {
+      a.send_pos[i] = -1;  // masked or out-of-range entries
+    }
+    if (++kk == g.K) {
+      kk = 0;
+      ++tok;
+    }
+  }
+  if (tid == 0)
+#pragma unroll
+    for (int j = 0; j < kDirectExperts; ++j) src_prefix[j][g.R] = total[j];
+  if (M == 0)
+    for (int s2 = tid; s2 < g.R; s2 += nth)
+#pragma unroll
+      for (int j = 0; j < kDirectExperts; ++j) src_prefix[j][s2] = 0;
+  __syncthreads();
+  const int ne = min(kDirectExperts, g.E - e0);
+  for (int x = tid; x < g.R * ne; x += nth) {
+    const int s2 = x / ne, j = x - s2 * ne;
+    a.cnt_expert[(int64_t)s2 * g.E + e0 + j] = src_prefix[j][s2 + 1] - src_prefix[j][s2];
+  }
+  if (tid < ne) {
+    a.recv_per_expert[e0 + tid] = src_prefix[tid][g.R];
+    a.expert_start[e0 + tid] = ll ? (e0 + tid) * rt : starts[e0 + tid];
+  }
+  // alignment padding rows of these segments
+  if (!ll && !msg && a.recv_src_idx && a.align > 1) {
+    for (int j = 0; j < ne; ++j) {
+      const int n = src_prefix[j][g.R], st = starts[e0 + j];
+      const int end = st + (n + a.align - 1) / a.align * a.align;
+      for (int r = st + n + tid; r < end; r += nth)
+        if (r < a.recv_cap) a.recv_src_idx[r] = -1;
+    }
+  }
+  if (!first) return;
+  // block 0: rows per rank, row bases and the error word
+  for (int d = tid; d <= g.R; d += nth) {
+    const int base = ll ? d * g.L * rt : starts[d * g.L];
+    a.row_base[d] = base;
+    if (d < g.R) a.rows[d] = ll ? g.L * rt : starts[(d + 1) * g.L] - base;
+  }
+  int bits = 0;
+  for (int i = tid; i < g.E; i += nth) {
+    const int n = hist[i];
+    if (ll && n > rt) bits |= EP_DEVERR_LL_OVERFLOW;
+    const int used = ll ? min(n, rt) : n;
+    const int64_t top = (ll ? (int64_t)i * rt : (int64_t)starts[i]) + used;
+    if (!msg && a.recv_src_idx && used > 0 && top > a.recv_cap) bits |= EP_DEVERR_CAPACITY;
+  }
+  if (bits) atomicOr(err_bits, bits);
+  __syncthreads();
+  if (tid == 0) *a.err = *err_bits;
+}
+
+__device__ void direct_rank_block(const LayoutArgs& a, int d, int* src_prefix) {
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int N = g.R * g.T;
+  const int per = (N + nth - 1) / nth;  // <= kDirectPer
+  const int lo = min(N, tid * per), hi = min(N, lo + per);
+  const int e_lo = d * g.L, e_hi = e_lo + g.L;  // experts on rank d
+  // bit q: token lo + q has an expert on rank d
+  uint32_t flags = 0;
+  for (int q = 0; q < hi - lo; ++q) {
+    const int32_t* ids = a.topk + (int64_t)(lo + q) * g.K;
+    int f = 0;
+    for (int k0 = 0; k0 < g.K; k0 += 8) {  // eight loads in flight at a time
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = k0 + j < g.K ? ids[k0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f |= v[j] >= e_lo && v[j] < e_hi;
+    }
+    flags |= (uint32_t)f << q;
+  }
+  const int cnt = __popc(flags);
+  int total;
+  int run = block_exclusive_scan(cnt, &total);
+  const int run0 = run;
+  int next_src = g.T > 0 ? (lo + g.T - 1) / g.T : 0;
+  for (int q = 0; q < hi - lo; ++q) {
+    if (lo + q == next_src * g.T) src_prefix[next_src++] = run;
+    run += (flags >> q) & 1;
+  }
+  if (tid == 0) src_prefix[g.R] = total;
+  if (N == 0)
+    for (int s2 = tid; s2 < g.R; s2 += nth) src_prefix[s2] = 0;
+  __syncthreads();
+  run = run0;
+  int src = g.T > 0 ? lo / g.T : 0, t = lo - src * g.T;
+  for (int q = 0; q < hi - lo; ++q) {
+    const int f = (flags >> q) & 1;
+    const int64_t at = (int64_t)(lo + q) * g.R + d;
+    a.in_rank[at] = (uint8_t)f;
+    if (a.send_head) a.send_head[at] = f ? run - src_prefix[src] : -1;
+    run += f;
+    if (++t == g.T) {
+      t = 0;
+      ++src;
+    }
+  }
+  for (int s2 = tid; s2 < g.R; s2 += nth) {
+    a.cnt_rank[s2 * g.R + d] = src_prefix[s2 + 1] - src_prefix[s2];
+    a.rpm[s2 * g.R + d] = src_prefix[s2 + 1];
+  }
+}
+
+__global__ __launch_bounds__(kDirectThreads) void layout_direct(LayoutArgs a) {
+  __shared__ int hist[2048];
+  __shared__ int starts[2049];
+  __shared__ int src_prefix[kDirectExperts][257];
+  __shared__ int err_bits;
+  const int eb = (a.g.E + kDirectExperts - 1) / kDirectExperts;
+  if ((int)blockIdx.x < eb)
+    direct_expert_block(a, blockIdx.x * kDirectExperts, hist, starts, src_prefix, &err_bits);
+  else
+    direct_rank_block(a, blockIdx.x - eb, src_prefix[0]);
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   const Geometry& g = a.g;
-  if (g.fused) {
-    const size_t lds = sizeof(int32_t) * ((size_t)16 * (g.E + g.R + g.tb * g.R) +
-                                          (size_t)(g.E + g.R) * g.NC + g.E + 1);
-    hipLaunchKernelGGL(layout_fused, dim3(1), dim3(1024), lds, stream, a);
+  if (g.direct && (int64_t)g.R * g.T * g.K <= (int64_t)kDirectPer * kDirectThreads) {
+    const int eb = (g.E + kDirectExperts - 1) / kDirectExperts;
+    hipLaunchKernelGGL(layout_direct, dim3(eb + g.R), dim3(kDirectThreads), 0, stream, a);
     return hipGetLastError();
   }
   // LDS per wavefront: expert and rank counters plus one batch of rows;
