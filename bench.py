@@ -72,7 +72,8 @@ def combine_bytes(w):
 
 def kernel_hash():
     h = hashlib.sha256()
-    for f in ["dispatch.hip", "combine.hip", "messages.hip", "quant.hpp", "ep_device.hpp"]:
+    for f in ["dispatch.hip", "combine.hip", "messages.hip", "receive.hip", "msg_format.hpp",
+              "quant.hpp", "ep_device.hpp"]:
         with open(os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -123,12 +124,26 @@ class Runner:
             table = self.msgs.table.cpu().numpy()
             nd = int(self.msgs.num_descriptors.item())
             msg_bytes = int(table[:, :, 2].sum())
+            n_msg = int((table[:, :, 2] > 0).sum())
+            # delivery into the receive arenas, then unpacking into the
+            # low-latency layout (E*R*T rows)
+            self.recv_cap = int(self.msgs.arena_base[1, -1].item())
+            self.recv_arena = torch.empty(self.recv_cap, dtype=torch.uint8, device=dev)
+            self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.unp = ep.unpack_buffers(self.p)
             lay = layout_bytes(w, 0)
             disp = 2 * w.H * w.N + 8 * w.K * w.N + msg_bytes + 64 * nd + 64 * w.R * w.R
-            self.bytes = {"layout": lay, "dispatch": disp}
-            self.kernels = {"dispatch": "msg_pack_fp8" if w.quant else "msg_pack_bf16"}
-            self.extra = {"messages": int((table[:, :, 2] > 0).sum()), "descriptors": nd,
-                          "message_bytes": msg_bytes}
+            cb = 2 if w.quant == ep.QUANT_NONE else 1
+            sb = {0: 0, 1: 4, 2: 1}[w.quant]
+            routed = int((topk >= 0).sum())
+            tokens_sent = int(table[:, :, 3].sum())
+            execute = 2 * msg_bytes + 64 * nd
+            unpack = (routed * (2 * (w.H * cb + w.G * sb) + 4) + tokens_sent * (4 * w.K + 4)
+                      + 32 * n_msg)
+            self.bytes = {"layout": lay, "dispatch": disp, "execute": execute, "unpack": unpack}
+            self.kernels = {"dispatch": "msg_pack_fp8" if w.quant else "msg_pack_bf16",
+                            "execute": "msg_exec_puts", "unpack": "msg_unpack"}
+            self.extra = {"messages": n_msg, "descriptors": nd, "message_bytes": msg_bytes}
             return
         if w.mode == ep.MODE_NORMAL:
             self.rows = int(self.lay.row_base[-1].item())  # untimed read-back of the receive size
@@ -151,24 +166,35 @@ class Runner:
                         "combine": "combine_rows"}
         self.extra = {}
 
-    def step(self, ev=None):
+    def phases(self):
+        """The step's calls in order, one per timed phase (built once)."""
+        if getattr(self, "_phases", None) is not None:
+            return self._phases
         ep, p = self.ep, self.p
-        if ev is not None:
-            ev[0].record()
-        ep.get_layout(p, self.topk, self.lay, self.ws)
-        if ev is not None:
-            ev[1].record()
+        ph = [("layout", lambda: ep.get_layout(p, self.topk, self.lay, self.ws))]
         if self.msgs is not None:
-            ep.dispatch(p, self.lay, self.x, msgs=self.msgs, topk_idx=self.topk,
-                        topk_weights=self.wt, ws=self.ws)
+            ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, msgs=self.msgs,
+                                                       topk_idx=self.topk, topk_weights=self.wt,
+                                                       ws=self.ws)))
+            ph.append(("execute", lambda: ep.messages_execute(p, self.msgs, self.recv_arena,
+                                                              self.err)))
+            ph.append(("unpack", lambda: ep.messages_unpack(p, self.msgs, self.recv_arena,
+                                                            self.lay.num_tokens_per_expert,
+                                                            *self.unp, self.err)))
         else:
-            ep.dispatch(p, self.lay, self.x, recv=self.recv, ws=self.ws)
+            ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
+                                                       ws=self.ws)))
+            ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, self.wt, self.out)))
+        self._phases = ph
+        return ph
+
+    def step(self, ev=None):
+        for i, (_, call) in enumerate(self.phases()):
+            if ev is not None:
+                ev[i].record()
+            call()
         if ev is not None:
-            ev[2].record()
-        if self.msgs is None:
-            ep.combine(p, self.lay, self.y, self.wt, self.out)
-        if ev is not None:
-            ev[3].record()
+            ev[-1].record()
 
     def run(self, steps, warmup):
         """Time `steps` whole steps with nothing else on the stream (the
@@ -185,15 +211,16 @@ class Runner:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / steps
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        n_ph = len(self.phases())
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         for i in range(steps):
             self.step(evs[i])
         torch.cuda.synchronize()
-        err = int(self.lay.err.item())
+        err = int(self.lay.err.item()) | (int(self.err.item()) if self.msgs is not None else 0)
         if err:
             raise RuntimeError(f"device error word {err}")
-        names = ["layout", "dispatch", "combine"][: len(self.bytes)]
+        names = [n for n, _ in self.phases()]
         ph = {k: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k in enumerate(names)}
         return ms, {k: float(np.mean(v)) for k, v in ph.items()}, \
             {k: float(np.median(v)) for k, v in ph.items()}

@@ -272,6 +272,75 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
   return EP_OK;
 }
 
+int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv_arena,
+                        int64_t recv_capacity, int32_t* err, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (p->mode != EP_MODE_MESSAGES) return EP_ERR_MODE;
+  if (!m || !err || !m->table || !m->arena_base || !m->num_descriptors) return EP_ERR_NULL;
+  if ((m->send_capacity > 0 && !m->send_arena) || (m->desc_capacity > 0 && !m->descriptors) ||
+      (recv_capacity > 0 && !recv_arena))
+    return EP_ERR_NULL;
+  if (!aligned(m->send_arena, 16) || !aligned(recv_arena, 16) || !aligned(m->descriptors, 16) ||
+      !aligned(m->table, 8) || !aligned(m->arena_base, 8) || !aligned(m->num_descriptors, 8) ||
+      !aligned(err, 4))
+    return EP_ERR_ALIGN;
+  if (m->send_capacity < 0 || m->desc_capacity < 0 || recv_capacity < 0) return EP_ERR_CAPACITY;
+  if (m->desc_capacity > 0x7fffffff) return EP_ERR_SHAPE;  // one block per descriptor piece
+  ep::ExecArgs a;
+  a.g = g;
+  a.region_bytes = p->region_bytes;
+  a.send = m->send_arena;
+  a.send_cap = m->send_capacity;
+  a.table = m->table;
+  a.arena_base = m->arena_base;
+  a.desc = m->descriptors;
+  a.desc_cap = m->desc_capacity;
+  a.num_desc = m->num_descriptors;
+  a.recv = recv_arena;
+  a.recv_cap = recv_capacity;
+  a.err = err;
+  if (ep::launch_execute(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
+int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t* recv_arena,
+                       int64_t recv_capacity, const int32_t* num_tokens_per_expert,
+                       const ep_recv* out, int32_t* recv_count, int32_t* recv_src_idx,
+                       int32_t* err, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (p->mode != EP_MODE_MESSAGES) return EP_ERR_MODE;
+  const int64_t rows = (int64_t)g.E * g.R * g.T;
+  if (!m || !m->table || !out || !err || !recv_count || !num_tokens_per_expert)
+    return EP_ERR_NULL;
+  if (rows > 0 && (!out->x || !recv_src_idx || (p->quant != EP_QUANT_NONE && !out->scales)))
+    return EP_ERR_NULL;
+  if (recv_capacity > 0 && !recv_arena) return EP_ERR_NULL;
+  if (!aligned(recv_arena, 16) || !aligned(out->x, 16) || !aligned(out->scales, 4) ||
+      !aligned(m->table, 8) || !aligned(num_tokens_per_expert, 4) || !aligned(recv_count, 4) ||
+      !aligned(recv_src_idx, 4) || !aligned(err, 4))
+    return EP_ERR_ALIGN;
+  if (recv_capacity < 0 || out->capacity < rows) return EP_ERR_CAPACITY;
+  ep::UnpackArgs a;
+  a.g = g;
+  a.quant = p->quant;
+  a.epoch = p->epoch;
+  a.arena = recv_arena;
+  a.recv_cap = recv_capacity;
+  a.table = m->table;
+  a.cnt_expert = num_tokens_per_expert;
+  a.recv_x = out->x;
+  a.recv_scales = out->scales;
+  a.recv_count = recv_count;
+  a.recv_src_idx = recv_src_idx;
+  a.err = err;
+  if (ep::launch_unpack(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
 int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y, int64_t y_rows,
                const float* topk_weights, uint16_t* out, void* stream) {
   Geometry g;

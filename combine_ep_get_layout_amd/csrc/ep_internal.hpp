@@ -110,4 +110,40 @@ struct MessageArgs {
 
 hipError_t launch_messages(const MessageArgs& a, hipStream_t stream);
 
+// Loopback execution of message mode's descriptors.
+struct ExecArgs {
+  Geometry g;
+  int64_t region_bytes;
+  const uint8_t* send;       // send arenas
+  int64_t send_cap;
+  const int64_t* table;      // [R][R][8]
+  const int64_t* arena_base; // [2][R+1]
+  const uint8_t* desc;       // [desc_cap][64]
+  int64_t desc_cap;
+  const int64_t* num_desc;
+  uint8_t* recv;             // receive arenas
+  int64_t recv_cap;
+  int32_t* err;
+};
+
+hipError_t launch_execute(const ExecArgs& a, hipStream_t stream);
+
+// Receiver: delivered messages -> low-latency layout.
+struct UnpackArgs {
+  Geometry g;
+  int quant;
+  uint32_t epoch;
+  const uint8_t* arena;        // receive arenas
+  int64_t recv_cap;
+  const int64_t* table;        // [R][R][8]
+  const int32_t* cnt_expert;   // [R][E]
+  void* recv_x;                // [E*R*T][H] bf16 or codes
+  void* recv_scales;           // [E][G][R*T]
+  int32_t* recv_count;         // [E]
+  int32_t* recv_src_idx;       // [E*R*T]
+  int32_t* err;
+};
+
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream);
+
 }  // namespace ep

@@ -24,35 +24,10 @@
 //               a fence) the completion flag, then the descriptors.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "msg_format.hpp"
 #include "quant.hpp"
 
 namespace ep {
-
-struct MsgSections {
-  int64_t off[5];  // section offsets within the body
-  int64_t len[5];  // unpadded section lengths
-  int64_t body;    // body bytes (sum of padded sections)
-};
-
-__host__ __device__ inline int64_t pad16(int64_t v) { return (v + 15) & ~(int64_t)15; }
-
-// Body of a message with n tokens: codes | scales | weights | ids | token.
-__host__ __device__ inline MsgSections msg_sections(int64_t n, int H, int K, int quant) {
-  MsgSections m;
-  const int64_t G = H / 128;
-  m.len[0] = n * H * (quant == EP_QUANT_NONE ? 2 : 1);
-  m.len[1] = n * G * (quant == EP_QUANT_FP8_F32 ? 4 : (quant == EP_QUANT_FP8_UE8M0 ? 1 : 0));
-  m.len[2] = n * K * 4;
-  m.len[3] = n * K * 4;
-  m.len[4] = n * 4;
-  int64_t o = 0;
-  for (int i = 0; i < 5; ++i) {
-    m.off[i] = o;
-    o += pad16(m.len[i]);
-  }
-  m.body = o;
-  return m;
-}
 
 // Number of pieces a put [la, la+len) -> [ra, ra+len) is cut into when no
 // piece may cross a multiple of rb on either side.
@@ -336,7 +311,6 @@ __global__ __launch_bounds__(256) void msg_pack_bf16(MessageArgs a, int V) {
   });
 }
 
-__device__ __forceinline__ uint32_t be32(uint32_t v) { return __builtin_bswap32(v); }
 
 // One 64-byte descriptor: control | remote address | data | zero pad.
 __device__ __forceinline__ void write_desc(uint8_t* dst, uint32_t wqe, uint32_t qpn,

@@ -1,0 +1,263 @@
+// Message delivery inside one GPU (loopback descriptor execution) and the
+// receiver that unpacks delivered messages into the low-latency layout.
+//
+// "ibgda_device.cuh" notes, sec. 1, and "GPU-Initiated Communication:
+// Dissecting Down to the Bone", WQE anatomy: a write descriptor names a
+// local (lkey, laddr) and a remote (rkey, raddr) address and a length; the
+// "wire" here is a copy between two arenas in HBM.  Same page, Ordering: the
+// store that announces a message (its completion flag) must become visible
+// after the message.  "Eaas_server" notes: the receiver reads a loaded
+// server's message once its flag has arrived.  "DeepEP" deep dive, sec. 1.2:
+// the packed low-latency layout the receiver fills (one block of R*T rows
+// per expert, recv_count); sec. 2.1: the per-expert counts ranks exchange
+// before the data, which give every source's first slot.
+//
+// Execute, two launches:
+//   1. every descriptor except the last one of each message (its flag), cut
+//      into pieces of at most kPieceBytes; one block per (descriptor, piece)
+//      copies with 16-byte vectors, four per thread in flight;
+//   2. one thread per message copies its flag.
+//   The launch boundary puts every payload and header before every flag.
+// Unpack, one launch: one block per (source, destination) message, one
+// wavefront per local expert of the destination.  Thread 0 checks the
+// header and the flag once (no waiting: a message that fails is reported
+// and skipped).  The wavefront walks the message's expert ids in (token, k)
+// order with one ballot per 64 entries; each match takes the next slot of
+// its expert after the slots of earlier sources, and the wavefront copies
+// the token's row and scales there.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+#include "msg_format.hpp"
+
+namespace ep {
+
+// One block of 1024 threads per descriptor piece of up to 2 MiB (a whole
+// descriptor at the default region size).  Measured on MI355X at the
+// 64-rank message workload: 0.395 ms against 0.42-0.47 ms for 256 KiB -
+// 1 MiB pieces of 256 - 512 threads (more blocks with nothing to copy) and
+// for non-temporal loads and stores.
+constexpr int64_t kPieceBytes = 2048 * 1024;
+constexpr int kMaxPieces = 64;
+constexpr int kExecThreads = 1024;
+
+struct Put {
+  int64_t src, dst, len;  // absolute offsets in the send / receive arenas
+  int s, d;
+};
+
+// Descriptor i (control | remote address | data | pad, big-endian fields).
+// Returns 0 when the put may run, else the error bit that rejects it.
+__device__ inline int read_put(const ExecArgs& a, int64_t i, Put* p) {
+  const u32x4* q = (const u32x4*)(a.desc + i * 64);
+  const u32x4 r = q[1], dt = q[2];
+  const uint64_t raddr = ((uint64_t)be32(r[0]) << 32) | be32(r[1]);
+  const uint32_t rkey = be32(r[2]);
+  const uint32_t len = be32(dt[0]);
+  const uint32_t lkey = be32(dt[1]);
+  const uint64_t laddr = ((uint64_t)be32(dt[2]) << 32) | be32(dt[3]);
+  const int R = a.g.R;
+  p->s = (int)(lkey >> 16);
+  p->d = (int)(rkey >> 16);
+  p->len = len;
+  if (p->s >= R || p->d >= R) return EP_DEVERR_MESSAGE;
+  const int64_t* send_base = a.arena_base;
+  const int64_t* recv_base = a.arena_base + R + 1;
+  const uint64_t send_sz = (uint64_t)(send_base[p->s + 1] - send_base[p->s]);
+  const uint64_t recv_sz = (uint64_t)(recv_base[p->d + 1] - recv_base[p->d]);
+  if (laddr > send_sz || len > send_sz - laddr || raddr > recv_sz || len > recv_sz - raddr)
+    return EP_DEVERR_CAPACITY;
+  p->src = send_base[p->s] + (int64_t)laddr;
+  p->dst = recv_base[p->d] + (int64_t)raddr;
+  if (p->src + p->len > a.send_cap || p->dst + p->len > a.recv_cap) return EP_DEVERR_CAPACITY;
+  return 0;
+}
+
+// Copies bytes [lo, hi) of a put with the threads of the block.
+__device__ inline void copy_range(const ExecArgs& a, const Put& p, int64_t lo, int64_t hi) {
+  const uint8_t* src = a.send + p.src;
+  uint8_t* dst = a.recv + p.dst;
+  if (((p.src | p.dst | lo | hi) & 15) == 0) {
+    // four vectors per thread in flight: loads of a round before its stores
+    const u32x4* s4 = (const u32x4*)(src + lo);
+    u32x4* d4 = (u32x4*)(dst + lo);
+    const int64_t nv = (hi - lo) / 16, step = blockDim.x;
+    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += 4 * step) {
+      u32x4 t[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t v = v0 + q * step;
+        t[q] = s4[v < nv ? v : nv - 1];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (v0 + q * step < nv) d4[v0 + q * step] = t[q];
+    }
+  } else {
+    for (int64_t o = lo + threadIdx.x; o < hi; o += blockDim.x) dst[o] = src[o];
+  }
+}
+
+__device__ inline int64_t live_descriptors(const ExecArgs& a) {
+  const int64_t n = *a.num_desc;
+  return n < a.desc_cap ? n : a.desc_cap;
+}
+
+// Launch 1: blockIdx.x = descriptor, blockIdx.y = piece.  Flags are left to
+// launch 2.
+__global__ __launch_bounds__(kExecThreads) void msg_exec_puts(ExecArgs a, int64_t piece) {
+  const int64_t i = blockIdx.x;
+  if (i >= live_descriptors(a)) return;
+  Put p;
+  const int bad = read_put(a, i, &p);
+  if (bad) {
+    if (blockIdx.y == 0 && threadIdx.x == 0) set_err(a.err, bad);
+    return;
+  }
+  const int64_t* row = a.table + ((int64_t)p.s * a.g.R + p.d) * 8;
+  if (i == row[5] + row[6] - 1) return;  // the message's flag
+  const int64_t lo = (int64_t)blockIdx.y * piece;
+  if (lo >= p.len) return;
+  const int64_t hi = lo + piece < p.len ? lo + piece : p.len;
+  copy_range(a, p, lo, hi);
+}
+
+// Launch 2: one thread per (s, d) message copies the last descriptor of the
+// message, its completion flag.
+__global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
+  const int R = a.g.R;
+  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= (int64_t)R * R) return;
+  const int64_t* row = a.table + m * 8;
+  if (row[3] <= 0 || row[6] <= 0) return;
+  const int64_t i = row[5] + row[6] - 1;
+  if (i >= live_descriptors(a)) return;
+  Put p;
+  const int bad = read_put(a, i, &p);
+  if (bad) {
+    set_err(a.err, bad);
+    return;
+  }
+  for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
+}
+
+// Unpack: blockIdx.x = s * R + d; wavefront w takes local experts w, w + waves, ...
+__global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
+  const Geometry& g = a.g;
+  const int R = g.R, L = g.L, E = g.E, K = g.K, H = g.H, G = g.G, T = g.T;
+  const int s = blockIdx.x / R, d = blockIdx.x % R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int64_t rt = (int64_t)R * T;
+  // recv_count of d's experts: written once, by the block of source 0
+  if (s == 0) {
+    for (int l = wave; l < L; l += nw) {
+      int64_t c = 0;
+      for (int s2 = lane; s2 < R; s2 += kWave) c += a.cnt_expert[(int64_t)s2 * E + d * L + l];
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+      if (lane == 0) a.recv_count[d * L + l] = (int32_t)c;
+    }
+  }
+  const int64_t* row = a.table + ((int64_t)s * R + d) * 8;
+  const int64_t n = row[3];
+  if (n <= 0) return;
+  const int64_t off = row[1], reg = row[2], body = row[4];
+  if (off < 0 || off + reg > a.recv_cap) {
+    if (threadIdx.x == 0) set_err(a.err, EP_DEVERR_CAPACITY);
+    return;
+  }
+  const MsgSections ms = msg_sections(n, H, K, a.quant);
+  const uint8_t* msg = a.arena + off;
+  __shared__ int ok;
+  if (threadIdx.x == 0) {
+    const u32x4 hd = *(const u32x4*)msg;
+    int good = hd[0] == (uint32_t)s && hd[1] == (uint32_t)d && hd[2] == (uint32_t)n &&
+               hd[3] == (uint32_t)body && body == ms.body && reg == 32 + body;
+    if (good) {
+      const u32x4 fl = *(const u32x4*)(msg + 16 + body);
+      good = fl[0] == a.epoch && fl[1] == 0u && fl[2] == 0u && fl[3] == 0u;
+    }
+    if (!good) set_err(a.err, EP_DEVERR_MESSAGE);
+    ok = good;
+  }
+  __syncthreads();
+  if (!ok) return;
+  const uint8_t* b = msg + 16;
+  const int32_t* ids = (const int32_t*)(b + ms.off[3]);
+  const int32_t* src_tok = (const int32_t*)(b + ms.off[4]);
+  const int cb = a.quant == EP_QUANT_NONE ? 2 : 1;
+  const int sb = a.quant == EP_QUANT_FP8_F32 ? 4 : (a.quant == EP_QUANT_FP8_UE8M0 ? 1 : 0);
+  const int64_t row_bytes = (int64_t)H * cb;
+  const int nvec = (int)(row_bytes / 16);
+  const int64_t nent = n * K;
+  for (int l = wave; l < L; l += nw) {
+    const int e = d * L + l;
+    int64_t run = 0;  // slots taken by earlier sources
+    for (int s2 = lane; s2 < s; s2 += kWave) run += a.cnt_expert[(int64_t)s2 * E + e];
+    for (int o = 32; o > 0; o >>= 1) run += __shfl_xor(run, o);
+    for (int64_t i0 = 0; i0 < nent; i0 += kWave) {
+      const int64_t i = i0 + lane;
+      const int id = i < nent ? ids[i] : -1;
+      uint64_t hits = __ballot(id == e);
+      while (hits) {  // in (token, k) order
+        const int hl = __builtin_ctzll(hits);
+        hits &= hits - 1;
+        const int64_t j = (i0 + hl) / K;
+        const int64_t pos = run++;
+        if (pos >= rt) {
+          if (lane == 0) set_err(a.err, EP_DEVERR_LL_OVERFLOW);
+          continue;
+        }
+        const int t = src_tok[j];
+        if (t < 0 || t >= T) {
+          if (lane == 0) set_err(a.err, EP_DEVERR_MESSAGE);
+          continue;
+        }
+        const int64_t r = (int64_t)e * rt + pos;
+        const u32x4* sv = (const u32x4*)(b + ms.off[0] + j * row_bytes);
+        u32x4* dv = (u32x4*)((uint8_t*)a.recv_x + r * row_bytes);
+        for (int v0 = lane; v0 < nvec; v0 += 8 * kWave) {  // eight vectors per lane in flight
+          u32x4 t[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) t[q] = sv[min(v0 + q * kWave, nvec - 1)];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (v0 + q * kWave < nvec) dv[v0 + q * kWave] = t[q];
+        }
+        if (sb == 4) {
+          const float* ss = (const float*)(b + ms.off[1]) + j * G;
+          for (int q = lane; q < G; q += kWave)
+            ((float*)a.recv_scales)[((int64_t)e * G + q) * rt + pos] = ss[q];
+        } else if (sb == 1) {
+          const uint8_t* ss = b + ms.off[1] + j * G;
+          for (int q = lane; q < G; q += kWave)
+            ((uint8_t*)a.recv_scales)[((int64_t)e * G + q) * rt + pos] = ss[q];
+        }
+        if (lane == 0) a.recv_src_idx[r] = (int32_t)((int64_t)s * T + t);
+      }
+    }
+  }
+}
+
+hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
+  const int R = a.g.R;
+  // pieces of at least kPieceBytes, at most kMaxPieces per descriptor (a
+  // descriptor never exceeds region_bytes)
+  int64_t piece = kPieceBytes;
+  const int64_t min_piece = pad16((a.region_bytes + kMaxPieces - 1) / kMaxPieces);
+  if (piece < min_piece) piece = min_piece;
+  const int64_t pieces = (a.region_bytes + piece - 1) / piece;
+  if (a.desc_cap > 0)
+    hipLaunchKernelGGL(msg_exec_puts, dim3((unsigned)a.desc_cap, (unsigned)pieces),
+                       dim3(kExecThreads), 0, st, a, piece);
+  const int64_t rr = (int64_t)R * R;
+  hipLaunchKernelGGL(msg_exec_flags, dim3((unsigned)((rr + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st) {
+  const int R = a.g.R;
+  int waves = a.g.L < 16 ? a.g.L : 16;
+  hipLaunchKernelGGL(msg_unpack, dim3((unsigned)R * R), dim3(kWave * waves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ep

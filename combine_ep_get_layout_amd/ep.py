@@ -19,10 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libep.so")
 
 MODE_NORMAL, MODE_LOW_LATENCY, MODE_MESSAGES = 0, 1, 2
 QUANT_NONE, QUANT_FP8_F32, QUANT_FP8_UE8M0 = 0, 1, 2
-DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY = 1, 2, 4
+DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY, DEVERR_MESSAGE = 1, 2, 4, 8
 
 EXPORTS = ["ep_workspace_bytes", "ep_max_recv_rows", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_status_string"]
+           "ep_combine", "ep_messages_execute", "ep_messages_unpack", "ep_status_string"]
 
 
 class EPError(RuntimeError):
@@ -84,6 +84,12 @@ def lib() -> ctypes.CDLL:
         l.ep_dispatch.restype = ctypes.c_int
         l.ep_combine.argtypes = [P, ctypes.POINTER(CLayout), _vp, ctypes.c_int64, _vp, _vp, _vp]
         l.ep_combine.restype = ctypes.c_int
+        l.ep_messages_execute.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64, _vp,
+                                          _vp]
+        l.ep_messages_execute.restype = ctypes.c_int
+        l.ep_messages_unpack.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64, _vp,
+                                         ctypes.POINTER(CRecv), _vp, _vp, _vp, _vp]
+        l.ep_messages_unpack.restype = ctypes.c_int
         l.ep_status_string.argtypes = [ctypes.c_int]
         l.ep_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -297,6 +303,60 @@ def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Ten
     y_rows = y.shape[0]
     _check(lib().ep_combine(ctypes.byref(p.c()), ctypes.byref(cl), _ptr(y), y_rows,
                             _ptr(topk_weights), _ptr(out), _stream(stream)), "ep_combine")
+
+
+def messages_execute(p: Problem, msgs: Messages, recv_arena: torch.Tensor, err: torch.Tensor,
+                     stream=None) -> None:
+    """Loopback delivery of the descriptors of `msgs` into `recv_arena`
+    (uint8; msgs.arena_base[1][R] bytes suffice).  Error bits are OR-ed
+    into err[0]."""
+    _need(p.mode == MODE_MESSAGES, "message-mode problem")
+    _need(recv_arena.dtype == torch.uint8, "recv_arena bytes")
+    _need(err.dtype == torch.int32 and err.numel() >= 1, "err int32")
+    _need(msgs.table.numel() == p.R * p.R * 8 and msgs.arena_base.numel() == 2 * (p.R + 1),
+          "message table / arena bases")
+    cm = msgs.c()
+    _check(lib().ep_messages_execute(ctypes.byref(p.c()), ctypes.byref(cm), _ptr(recv_arena),
+                                     recv_arena.numel(), _ptr(err), _stream(stream)),
+           "ep_messages_execute")
+
+
+def unpack_buffers(p: Problem, device="cuda") -> tuple[Recv, torch.Tensor, torch.Tensor]:
+    """Low-latency receive buffers for messages_unpack: (rows and scales
+    [E*R*T], recv_count [E], recv_src_idx [E*R*T] filled with -1)."""
+    rows = p.E * p.R * p.T
+    recv = Recv(p, rows, device=device)
+    count = torch.zeros(p.E, dtype=torch.int32, device=device)
+    src = torch.full((max(rows, 1),), -1, dtype=torch.int32, device=device)
+    return recv, count, src
+
+
+def messages_unpack(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
+                    num_tokens_per_expert: torch.Tensor, out: Recv, recv_count: torch.Tensor,
+                    recv_src_idx: torch.Tensor, err: torch.Tensor, stream=None) -> None:
+    """Receiver: checks every delivered message and unpacks it into the
+    low-latency layout `out` (capacity >= E*R*T).  Error bits are OR-ed into
+    err[0]."""
+    R, T, E = p.R, p.T, p.E
+    rows = E * R * T
+    _need(p.mode == MODE_MESSAGES, "message-mode problem")
+    _need(recv_arena.dtype == torch.uint8, "recv_arena bytes")
+    _need(num_tokens_per_expert.dtype == torch.int32 and num_tokens_per_expert.numel() == R * E,
+          "num_tokens_per_expert [R][E] int32")
+    _need(out.capacity >= rows and out.x.shape[0] >= rows and out.x.shape[1] == p.H,
+          "out rows [E*R*T][H]")
+    _need(out.x.element_size() == (2 if p.quant == QUANT_NONE else 1), "out row element size")
+    if p.quant != QUANT_NONE:
+        _need(out.scales is not None and out.scales.numel() >= p.G * rows, "out scales")
+    _need(recv_count.dtype == torch.int32 and recv_count.numel() == E, "recv_count [E]")
+    _need(recv_src_idx.dtype == torch.int32 and recv_src_idx.numel() >= rows, "recv_src_idx")
+    _need(err.dtype == torch.int32 and err.numel() >= 1, "err int32")
+    _need(msgs.table.numel() == R * R * 8, "message table")
+    cm, cr = msgs.c(), out.c()
+    _check(lib().ep_messages_unpack(ctypes.byref(p.c()), ctypes.byref(cm), _ptr(recv_arena),
+                                    recv_arena.numel(), _ptr(num_tokens_per_expert),
+                                    ctypes.byref(cr), _ptr(recv_count), _ptr(recv_src_idx),
+                                    _ptr(err), _stream(stream)), "ep_messages_unpack")
 
 
 def messages_capacity(p: Problem, counts=None) -> tuple[int, int]:

@@ -103,7 +103,7 @@ def main():
             d = json.load(open(args.json))
         for k, v in traffic.items():
             for short in ("dispatch_copy", "combine_rows", "dispatch_fp8", "msg_pack_fp8",
-                          "msg_pack_bf16"):
+                          "msg_pack_bf16", "msg_exec_puts", "msg_unpack"):
                 if short in k:
                     d[f"{args.workload}:{short}"] = {"hbm_bytes_per_launch": round(v), "kernel": k,
                                                      "kernel_hash": kernel_hash(),

@@ -85,6 +85,8 @@ extern "C" {
 #define EP_DEVERR_TOPK_RANGE 1  /* a topk_idx entry outside [-1, E): entry skipped */
 #define EP_DEVERR_LL_OVERFLOW 2 /* low-latency position >= R*T (duplicate ids): skipped */
 #define EP_DEVERR_CAPACITY 4    /* a row or byte offset past the caller's capacity: skipped */
+#define EP_DEVERR_MESSAGE 8     /* a descriptor names a rank outside [0, R), or a received
+                                   message's header or completion flag does not match: skipped */
 
 typedef struct ep_problem {
   int32_t num_ranks;        /* R                                           */
@@ -196,6 +198,45 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
  * Normal / low-latency modes. */
 int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y,
                int64_t y_rows, const float* topk_weights, uint16_t* out, void* stream);
+
+/* Loopback delivery of message mode's descriptors ("ibgda_device.cuh" notes,
+ * sec. 1; "GPU-Initiated Communication: Dissecting Down to the Bone", WQE
+ * anatomy and Ordering).  Descriptor i (i < min(*m->num_descriptors,
+ * m->desc_capacity)) copies its length of bytes from byte laddr of rank
+ * (lkey >> 16)'s send arena to byte raddr of rank (rkey >> 16)'s receive
+ * arena, the arena bases taken from m->arena_base (receive arena of rank d
+ * = recv_arena[arena_base[1][d] ...]).  The last descriptor of every
+ * message (m->table: first index + count - 1), its completion flag, is
+ * copied in a second launch, after every payload and header.
+ * recv_arena: [recv_capacity] bytes, 16-byte aligned (arena_base[1][R]
+ * bytes suffice).  Errors are OR-ed into *err (not reset):
+ * EP_DEVERR_MESSAGE for a rank outside [0, R), EP_DEVERR_CAPACITY for a put
+ * past either rank's arena or either buffer; such a put is skipped.
+ * p->mode must be EP_MODE_MESSAGES. */
+int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv_arena,
+                        int64_t recv_capacity, int32_t* err, void* stream);
+
+/* Receiver ("Eaas_server" notes; "DeepEP" sec. 1.2 and 2.1).  For every
+ * (s, d) with a message (m->table[s][d]: token count n > 0), checks the
+ * header {s, d, n, body bytes} and the completion flag {epoch, 0, 0, 0} at
+ * the message's receive offset (a mismatch sets EP_DEVERR_MESSAGE and the
+ * message is skipped; nothing waits), then unpacks it into the low-latency
+ * layout, exactly as low-latency dispatch of the same routing stores it:
+ * the message's entry (token j, k) with expert e of rank d takes slot
+ *   pos = sum_{s' < s} num_tokens_per_expert[s'][e]
+ *         + (earlier entries of the message with expert e),
+ * row e*R*T + pos of out->x (codes or bf16 row), scales at
+ * [(e*G + g)*R*T + pos], recv_src_idx[row] = s*T + t (t read from the
+ * message).  recv_count[e] = sum_s num_tokens_per_expert[s][e].  Rows not
+ * filled are left as they were.  pos >= R*T sets EP_DEVERR_LL_OVERFLOW; a
+ * message past recv_capacity sets EP_DEVERR_CAPACITY; errors are OR-ed into
+ * *err.  out->capacity >= E*R*T; recv_src_idx: [E*R*T]; recv_count: [E];
+ * num_tokens_per_expert: [R][E] (ep_get_layout's).  p->mode must be
+ * EP_MODE_MESSAGES (p->quant, p->epoch describe the messages). */
+int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t* recv_arena,
+                       int64_t recv_capacity, const int32_t* num_tokens_per_expert,
+                       const ep_recv* out, int32_t* recv_count, int32_t* recv_src_idx,
+                       int32_t* err, void* stream);
 
 /* Static text for a status code. */
 const char* ep_status_string(int status);

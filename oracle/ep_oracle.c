@@ -615,3 +615,125 @@ int orc_messages(const orc_problem* p, const uint16_t* x, const int32_t* topk,
   free(rows); free(rbase);
   return err;
 }
+
+/* ---- message delivery (loopback) and receive -------------------------- */
+
+static uint32_t get_be32(const uint8_t* b) {
+  return ((uint32_t)b[0] << 24) | ((uint32_t)b[1] << 16) | ((uint32_t)b[2] << 8) | b[3];
+}
+static uint64_t get_be64(const uint8_t* b) {
+  return ((uint64_t)get_be32(b) << 32) | get_be32(b + 4);
+}
+static uint32_t get_le32(const uint8_t* b) {
+  return (uint32_t)b[0] | ((uint32_t)b[1] << 8) | ((uint32_t)b[2] << 16) | ((uint32_t)b[3] << 24);
+}
+
+/* [IBGDA] sec. 1 and [GIC] WQE anatomy: a write descriptor names the local
+ * (lkey, laddr) and remote (rkey, raddr) addresses and the length; the
+ * loopback "wire" copies the bytes.  Field offsets are this library's own
+ * descriptor format (see orc_messages). */
+int orc_messages_execute(const orc_problem* p, const uint8_t* send_arena, int64_t send_cap,
+                         const int64_t* arena_base, const uint8_t* desc, int64_t num_desc,
+                         uint8_t* recv_arena, int64_t recv_cap) {
+  const int R = p->R;
+  const int64_t* send_base = arena_base;
+  const int64_t* recv_base = arena_base + (R + 1);
+  int err = 0;
+  for (int64_t i = 0; i < num_desc; ++i) {
+    const uint8_t* dsc = desc + i * 64;
+    const uint64_t raddr = get_be64(dsc + 16);
+    const uint32_t rkey = get_be32(dsc + 24);
+    const uint32_t len = get_be32(dsc + 32);
+    const uint32_t lkey = get_be32(dsc + 36);
+    const uint64_t laddr = get_be64(dsc + 40);
+    const uint32_t s = lkey >> 16, d = rkey >> 16;
+    if (s >= (uint32_t)R || d >= (uint32_t)R) {
+      err |= ORC_ERR_MESSAGE;
+      continue;
+    }
+    const int64_t src = send_base[s] + (int64_t)laddr, dst = recv_base[d] + (int64_t)raddr;
+    if (src + len > send_base[s + 1] || src + len > send_cap || dst + len > recv_base[d + 1] ||
+        dst + len > recv_cap) {
+      err |= ORC_ERR_CAPACITY;
+      continue;
+    }
+    memcpy(recv_arena + dst, send_arena + src, len);
+  }
+  return err;
+}
+
+/* [EAAS] (the receiver reads a loaded server's message once its completion
+ * flag has arrived) and [DEEP] sec. 1.2 (low-latency packed layout, one
+ * block of R*T rows per expert, recv_count).  Slots follow the stable
+ * (source, token, k) order pinned for low-latency dispatch; the receiver
+ * learns the per-source expert counts from the count exchange of [DEEP]
+ * sec. 2.1 (cnt_expert), and everything else from the message bytes. */
+int orc_messages_unpack(const orc_problem* p, const uint8_t* recv_arena, int64_t recv_cap,
+                        const int64_t* table, const int32_t* cnt_expert, void* recv,
+                        void* scales, int32_t* recv_count, int32_t* recv_src_idx) {
+  const int R = p->R, T = p->T, H = p->H, E = p->E, K = p->K, L = E / R, G = H / 128;
+  const int64_t RT = (int64_t)R * T;
+  const int cb = p->quant == ORC_Q_NONE ? 2 : 1;
+  const int sb = p->quant == ORC_Q_FP8_F32 ? 4 : (p->quant == ORC_Q_FP8_UE8M0 ? 1 : 0);
+  int err = 0;
+  for (int e = 0; e < E; ++e) {
+    int64_t n = 0;
+    for (int s = 0; s < R; ++s) n += cnt_expert[(int64_t)s * E + e];
+    recv_count[e] = (int32_t)n;
+  }
+  int64_t* run = (int64_t*)malloc(sizeof(int64_t) * (L > 0 ? L : 1));
+  for (int d = 0; d < R; ++d) {
+    for (int s = 0; s < R; ++s) {
+      const int64_t* row = table + ((int64_t)s * R + d) * 8;
+      const int64_t n = row[3];
+      if (n <= 0) continue;
+      const int64_t off = row[1], region = row[2], body = row[4];
+      if (off < 0 || off + region > recv_cap) {
+        err |= ORC_ERR_CAPACITY;
+        continue;
+      }
+      const uint8_t* m = recv_arena + off;
+      int ok = get_le32(m) == (uint32_t)s && get_le32(m + 4) == (uint32_t)d &&
+               get_le32(m + 8) == (uint32_t)n && get_le32(m + 12) == (uint32_t)body &&
+               get_le32(m + 16 + body) == p->epoch && get_le32(m + 20 + body) == 0 &&
+               get_le32(m + 24 + body) == 0 && get_le32(m + 28 + body) == 0;
+      if (!ok) {
+        err |= ORC_ERR_MESSAGE;
+        continue;
+      }
+      int64_t sec[6];
+      orc_msg_body_bytes(p, n, sec);
+      const uint8_t* b = m + 16;
+      /* slots of earlier sources, per local expert */
+      for (int l = 0; l < L; ++l) {
+        int64_t base = 0;
+        for (int s2 = 0; s2 < s; ++s2) base += cnt_expert[(int64_t)s2 * E + d * L + l];
+        run[l] = base;
+      }
+      for (int64_t j = 0; j < n; ++j) {
+        const uint32_t t = get_le32(b + sec[4] + j * 4);
+        for (int k = 0; k < K; ++k) {
+          const int32_t e = (int32_t)get_le32(b + sec[3] + (j * K + k) * 4);
+          if (e < 0 || e >= E || e / L != d) continue;
+          const int64_t pos = run[e - d * L]++;
+          if (pos >= RT) {
+            err |= ORC_ERR_LL_OVERFLOW;
+            continue;
+          }
+          if (t >= (uint32_t)T) {
+            err |= ORC_ERR_MESSAGE;
+            continue;
+          }
+          const int64_t r = (int64_t)e * RT + pos;
+          memcpy((uint8_t*)recv + r * H * cb, b + sec[0] + j * H * cb, (size_t)H * cb);
+          for (int g = 0; g < G && sb > 0; ++g)
+            memcpy((uint8_t*)scales + (((int64_t)e * G + g) * RT + pos) * sb,
+                   b + sec[1] + (j * G + g) * sb, (size_t)sb);
+          recv_src_idx[r] = (int32_t)((int64_t)s * T + t);
+        }
+      }
+    }
+  }
+  free(run);
+  return err;
+}

@@ -59,6 +59,7 @@ extern "C" {
 #define ORC_ERR_TOPK_RANGE 1  /* an index outside [-1, E)                    */
 #define ORC_ERR_LL_OVERFLOW 2 /* low-latency position >= R*T                  */
 #define ORC_ERR_CAPACITY 4    /* output buffer smaller than the data          */
+#define ORC_ERR_MESSAGE 8     /* a descriptor or received message is malformed */
 
 typedef struct {
   int32_t R;        /* simulated ranks                                     */
@@ -136,6 +137,33 @@ int orc_messages(const orc_problem* p, const uint16_t* x, const int32_t* topk,
                  int64_t* table /*[R][R][8]*/, int64_t* arena_base /*[2][R+1]*/,
                  uint8_t* desc /*[desc_cap][64]*/, int64_t desc_cap,
                  int64_t* num_desc);
+
+/* ---- message delivery (loopback) and receive ------------------------- */
+/* Executes the write descriptors in order: each copies its length of bytes
+ * from byte laddr of source rank (lkey >> 16)'s send arena to byte raddr of
+ * destination rank (rkey >> 16)'s receive arena (arena bases from
+ * arena_base).  A descriptor naming a rank outside [0, R) sets
+ * ORC_ERR_MESSAGE; one reaching past either rank's arena or the buffers
+ * sets ORC_ERR_CAPACITY; neither is executed.                              */
+int orc_messages_execute(const orc_problem* p, const uint8_t* send_arena, int64_t send_cap,
+                         const int64_t* arena_base, const uint8_t* desc, int64_t num_desc,
+                         uint8_t* recv_arena, int64_t recv_cap);
+
+/* Receiver: for every destination d and source s with a message (table
+ * [s][d]), checks the header {s, d, n, body} and the completion flag
+ * {epoch, 0, 0, 0} in the receive arena (mismatch: ORC_ERR_MESSAGE, the
+ * message is skipped) and unpacks its tokens into the low-latency layout:
+ * the entry (token j, k) of the message with expert e on d gets slot
+ *   pos = sum_{s' < s} cnt_expert[s'][e] + (entries of the message before it
+ *         with expert e),
+ * i.e. (source, token, k) order, row = e*(R*T) + pos; codes/rows and scales
+ * are stored as low-latency dispatch stores them, recv_src_idx[row] =
+ * s*T + t (t from the message), recv_count[e] = sum_s cnt_expert[s][e].
+ * pos >= R*T sets ORC_ERR_LL_OVERFLOW (not stored).                         */
+int orc_messages_unpack(const orc_problem* p, const uint8_t* recv_arena, int64_t recv_cap,
+                        const int64_t* table /*[R][R][8]*/, const int32_t* cnt_expert /*[R][E]*/,
+                        void* recv /*[E*R*T][H] bf16 or codes*/, void* scales,
+                        int32_t* recv_count /*[E]*/, int32_t* recv_src_idx /*[E*R*T]*/);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ _LIB = os.path.join(_HERE, "libep_oracle.so")
 
 MODE_NORMAL, MODE_LL, MODE_MSG = 0, 1, 2
 Q_NONE, Q_FP8_F32, Q_FP8_UE8M0 = 0, 1, 2
-ERR_TOPK_RANGE, ERR_LL_OVERFLOW, ERR_CAPACITY = 1, 2, 4
+ERR_TOPK_RANGE, ERR_LL_OVERFLOW, ERR_CAPACITY, ERR_MESSAGE = 1, 2, 4, 8
 
 
 def build(force: bool = False) -> str:
@@ -84,6 +84,10 @@ def lib():
         _lib.orc_msg_body_bytes.restype = i64
         _lib.orc_messages.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
         _lib.orc_messages.restype = ctypes.c_int
+        _lib.orc_messages_execute.argtypes = [P, vp, i64, vp, vp, i64, vp, i64]
+        _lib.orc_messages_execute.restype = ctypes.c_int
+        _lib.orc_messages_unpack.argtypes = [P, vp, i64, vp, vp, vp, vp, vp, vp]
+        _lib.orc_messages_unpack.restype = ctypes.c_int
     return _lib
 
 
@@ -288,3 +292,49 @@ def messages(p: Problem, x: np.ndarray, topk: np.ndarray, w: np.ndarray,
                              send_cap, _ptr(table), _ptr(base), _ptr(desc), desc_cap, _ptr(nd))
     n = int(nd[0])
     return Messages(err, arena[:send_cap], table, base, desc[:min(n, desc_cap)], n)
+
+
+def messages_execute(p: Problem, m: Messages, recv_cap: int, recv_arena: np.ndarray | None = None):
+    """Executes the descriptors of `m` (loopback) into a receive arena of
+    recv_cap bytes (fresh zeros unless `recv_arena` is given, which is
+    updated in place).  Returns (err, recv_arena)."""
+    if recv_arena is None:
+        recv_arena = np.zeros(max(recv_cap, 1), np.uint8)
+    desc = np.ascontiguousarray(m.desc, np.uint8)
+    err = lib().orc_messages_execute(ctypes.byref(p.c()), _ptr(m.send_arena), m.send_arena.size,
+                                     _ptr(m.arena_base), _ptr(desc), desc.shape[0],
+                                     _ptr(recv_arena), recv_cap)
+    return err, recv_arena
+
+
+@dataclass
+class Unpacked:
+    err: int
+    recv: np.ndarray          # [E*R*T][H] uint16 (bf16) or uint8 codes
+    scales: np.ndarray | None  # [E][G][R*T] float32 or uint8, flattened
+    recv_count: np.ndarray    # [E] int32
+    recv_src_idx: np.ndarray  # [E*R*T] int32, -1 where not written
+
+
+def messages_unpack(p: Problem, recv_arena: np.ndarray, table: np.ndarray,
+                    cnt_expert: np.ndarray, fill_codes: int = 0) -> Unpacked:
+    """Receiver: unpacks every valid message of the receive arena into the
+    low-latency layout.  Rows and scales not written keep `fill_codes` (bytes)."""
+    R, T, H, E = p.R, p.T, p.H, p.E
+    rows = E * R * T
+    if p.quant == Q_NONE:
+        recv = np.full((rows, H), fill_codes * 0x0101, np.uint16)
+        scales = None
+    else:
+        recv = np.full((rows, H), fill_codes, np.uint8)
+        dt = np.float32 if p.quant == Q_FP8_F32 else np.uint8
+        scales = np.zeros(max(p.G * rows, 1), dt)
+        scales.view(np.uint8)[:] = fill_codes
+    cnt = np.zeros(E, np.int32)
+    src = np.full(max(rows, 1), -1, np.int32)
+    arena = np.ascontiguousarray(recv_arena, np.uint8)
+    err = lib().orc_messages_unpack(ctypes.byref(p.c()), _ptr(arena), arena.size,
+                                    _ptr(np.ascontiguousarray(table, np.int64)),
+                                    _ptr(np.ascontiguousarray(cnt_expert, np.int32)),
+                                    _ptr(recv), _ptr(scales), _ptr(cnt), _ptr(src))
+    return Unpacked(err, recv, scales, cnt, src[:rows])

@@ -1,0 +1,192 @@
+"""GPU parity of message delivery (ep_messages_execute) and the receiver
+(ep_messages_unpack) against the oracle, through the C ABI.
+
+Small problems: the whole receive arena and every unpacked buffer (rows,
+scales, recv_src_idx, recv_count) are compared byte for byte with the
+oracle, both sides starting from the same fill values; the unpacked layout
+also equals the GPU's own low-latency dispatch of the same routing.
+Corrupted flags, headers and descriptors are rejected identically.
+The 64-rank message workload: the whole receive arena against the oracle,
+and sampled unpacked tokens against the oracle's quantisation of each
+token on its own."""
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_layout_amd import ep, inputs
+from oracle import oracle as orc
+from gpu_util import DEV, gpu_layout, h, problems, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, R, T, H, E, K, quant, region bytes, masked fraction, duplicate fraction
+    ("r1", 1, 9, 128, 4, 2, ep.QUANT_FP8_F32, 256, 0.0, 0.0),
+    ("r2_small_regions", 2, 17, 256, 8, 3, ep.QUANT_FP8_F32, 64, 0.2, 0.0),
+    ("r3_bf16", 3, 12, 128, 6, 2, ep.QUANT_NONE, 4096, 0.0, 0.0),
+    ("r4_ue8m0", 4, 20, 256, 16, 4, ep.QUANT_FP8_UE8M0, 512, 0.1, 0.3),
+    ("r5", 5, 7, 384, 10, 5, ep.QUANT_FP8_F32, 2 << 20, 0.0, 0.0),
+    ("r8_wide", 8, 40, 1024, 64, 8, ep.QUANT_FP8_F32, 8192, 0.05, 0.0),
+    ("r16_many_local", 16, 24, 256, 512, 6, ep.QUANT_FP8_F32, 1024, 0.0, 0.0),
+    ("r4_bf16_dups", 4, 33, 128, 8, 8, ep.QUANT_NONE, 128, 0.1, 0.4),
+]
+FILL = 0x5C
+
+
+def run_gpu(w, p, topk, x, wt):
+    """Layout, pack, execute and unpack on the GPU; returns every buffer."""
+    gl, ws = gpu_layout(p, topk)
+    send_cap, desc_cap = ep.messages_capacity(p, h(gl.num_tokens_per_rank))
+    msgs = ep.Messages(p, send_cap, desc_cap)
+    ep.dispatch(p, gl, torch.from_numpy(x).view(torch.bfloat16).to(DEV), msgs=msgs,
+                topk_idx=torch.from_numpy(topk).to(DEV), topk_weights=torch.from_numpy(wt).to(DEV),
+                ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(gl.err)[0]) == 0
+    recv_cap = int(h(msgs.arena_base)[1, -1])
+    arena = torch.full((recv_cap + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_execute(p, msgs, arena[:recv_cap], err)
+    out, cnt, src = ep.unpack_buffers(p)
+    out.x.view(torch.uint8).fill_(FILL)
+    if out.scales is not None:
+        out.scales.view(torch.uint8).fill_(FILL)
+    ep.messages_unpack(p, msgs, arena[:recv_cap], gl.num_tokens_per_expert, out, cnt, src, err)
+    torch.cuda.synchronize()
+    return gl, ws, msgs, arena, recv_cap, out, cnt, src, err
+
+
+def oracle_side(w, po, topk, x, wt, send_cap, desc_cap, recv_cap, cnt_expert):
+    om = orc.messages(po, x, topk, wt, send_cap, desc_cap)
+    assert om.err == 0
+    arena = np.full(recv_cap + 64, 0xA5, np.uint8)
+    e1, arena = orc.messages_execute(po, om, recv_cap, arena)
+    u = orc.messages_unpack(po, arena[:recv_cap], om.table, cnt_expert, fill_codes=FILL)
+    return om, arena, e1, u
+
+
+def compare_unpacked(w, out, cnt, src, u):
+    rows = w.E * w.R * w.T
+    g = h(out.x.view(torch.uint16) if w.quant == ep.QUANT_NONE else out.x)[:rows]
+    assert np.array_equal(g, u.recv)
+    if w.quant != ep.QUANT_NONE:
+        gs = h(out.scales.view(torch.uint8))[: u.scales.view(np.uint8).size]
+        assert np.array_equal(gs, u.scales.view(np.uint8))
+    assert np.array_equal(h(cnt), u.recv_count)
+    assert np.array_equal(h(src)[:rows], u.recv_src_idx)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_execute_and_unpack_match_oracle(case):
+    name, R, T, H, E, K, quant, rb, mfrac, dfrac = case
+    say("receive", name)
+    w = inputs.small(f"recv_{name}", R=R, T=T, H=H, E=E, K=K, mode=ep.MODE_MESSAGES, quant=quant,
+                     seed=61, region_bytes=rb, epoch=5)
+    topk = inputs.gen_topk(w)
+    if mfrac or dfrac:
+        topk = inputs.masked_topk(w, topk, mfrac, dfrac, seed=3)
+    x, wt = inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt)
+    om, oarena, e1, u = oracle_side(w, po, topk, x, wt, msgs.send_capacity, msgs.desc_capacity,
+                                    recv_cap, h(gl.num_tokens_per_expert))
+    assert e1 == 0
+    assert int(h(err)[0]) == u.err
+    assert np.array_equal(h(arena), oarena)  # the whole arena, padding and canary tail included
+    compare_unpacked(w, out, cnt, src, u)
+    # the unpacked layout is what low-latency dispatch of the same routing stores
+    pl = ep.Problem(R, T, H, E, K, mode=ep.MODE_LOW_LATENCY, quant=quant)
+    ll, lws = gpu_layout(pl, topk)
+    rl = ep.Recv(pl, E * R * T)
+    ep.dispatch(pl, ll, torch.from_numpy(x).view(torch.bfloat16).to(DEV), recv=rl, ws=lws)
+    torch.cuda.synchronize()
+    sp = h(ll.send_pos)
+    rows = torch.from_numpy(np.unique(sp[sp >= 0]).astype(np.int64)).to(DEV)
+    assert torch.equal(out.x[rows], rl.x[rows])
+    assert torch.equal(src[rows], ll.recv_src_idx[rows])
+    assert torch.equal(cnt, ll.recv_tokens_per_expert)
+    assert int(h(ll.err)[0]) == int(h(err)[0])
+
+
+def test_unpack_rejects_corrupt_flag_and_header_like_the_oracle():
+    w = inputs.small("recv_bad", R=4, T=20, H=256, E=16, K=4, mode=ep.MODE_MESSAGES,
+                     quant=ep.QUANT_FP8_F32, seed=71, region_bytes=512, epoch=9)
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt)
+    assert int(h(err)[0]) == 0
+    table = h(msgs.table)
+    t12, t30 = table[1, 2], table[3, 0]
+    assert t12[3] > 0 and t30[3] > 0
+    bad = arena.clone()
+    bad[int(t12[1] + 16 + t12[4])] ^= 1  # stale flag
+    bad[int(t30[1] + 8)] ^= 1            # wrong token count in the header
+    out2, cnt2, src2 = ep.unpack_buffers(p)
+    out2.x.fill_(FILL)
+    out2.scales.view(torch.uint8).fill_(FILL)
+    err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_unpack(p, msgs, bad[:recv_cap], gl.num_tokens_per_expert, out2, cnt2, src2, err2)
+    torch.cuda.synchronize()
+    u = orc.messages_unpack(po, h(bad)[:recv_cap], table, h(gl.num_tokens_per_expert),
+                            fill_codes=FILL)
+    assert u.err == orc.ERR_MESSAGE and int(h(err2)[0]) == ep.DEVERR_MESSAGE
+    compare_unpacked(w, out2, cnt2, src2, u)
+
+
+def test_execute_rejects_corrupt_descriptor_like_the_oracle():
+    w = inputs.small("recv_desc", R=2, T=17, H=256, E=8, K=3, mode=ep.MODE_MESSAGES,
+                     quant=ep.QUANT_FP8_F32, seed=72, region_bytes=64, epoch=3)
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt)
+    nd = int(h(msgs.num_descriptors)[0])
+    msgs.descriptors[1, 36] = 0x7F  # source rank out of range (a payload piece)
+    arena2 = torch.full((recv_cap + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_execute(p, msgs, arena2[:recv_cap], err2)
+    torch.cuda.synchronize()
+    om = orc.Messages(0, h(msgs.send_arena), h(msgs.table), h(msgs.arena_base),
+                      h(msgs.descriptors)[:nd], nd)
+    e, oarena = orc.messages_execute(po, om, recv_cap, np.full(recv_cap + 64, 0xA5, np.uint8))
+    assert e == orc.ERR_MESSAGE and int(h(err2)[0]) == ep.DEVERR_MESSAGE
+    assert np.array_equal(h(arena2), oarena)
+
+
+def test_workload_messages_delivery_and_unpack():
+    """R64 T256 H7168 E256 top-8 (0.94 GB of messages): the whole receive
+    arena against the oracle; recv_count and recv_src_idx of every row
+    against the oracle's low-latency layout; codes and scales of sampled
+    tokens against the oracle's quantisation of each token alone."""
+    w = inputs.WORKLOADS["messages"]
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    say("receive workload: GPU")
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt)
+    assert int(h(err)[0]) == 0
+    say("receive workload: oracle pack + execute")
+    om = orc.messages(po, x, topk, wt, msgs.send_capacity, msgs.desc_capacity)
+    _, oarena = orc.messages_execute(po, om, recv_cap, np.full(recv_cap + 64, 0xA5, np.uint8))
+    assert np.array_equal(h(arena), oarena)
+    del oarena
+    pl = orc.Problem(w.R, w.T, w.H, w.E, w.K, mode=orc.MODE_LL, quant=w.quant)
+    ol = orc.layout(pl, topk)
+    assert np.array_equal(h(cnt), ol.recv_tokens_per_expert)
+    g_src = h(src)
+    filled = ol.recv_src_idx >= 0
+    assert np.array_equal(g_src[filled], ol.recv_src_idx[filled])
+    assert (g_src[~filled] == -1).all()
+    # sampled tokens: every routed row of the token holds its codes and scales
+    rng = np.random.default_rng(5)
+    RT, G = w.R * w.T, w.G
+    p1 = orc.Problem(1, 1, w.H, 1, 1, quant=w.quant)
+    for st in rng.choice(w.R * w.T, 48, replace=False):
+        s, t = divmod(int(st), w.T)
+        _, codes, scales = orc.dispatch(p1, x[s, t][None, None], np.zeros((1, 1, 1), np.int32),
+                                        np.zeros((1, 1, 1), np.int32), 1)
+        for r in ol.send_pos[s, t]:
+            if r < 0:
+                continue
+            e, pos = divmod(int(r), RT)
+            assert np.array_equal(h(out.x[r]), codes[0])
+            gi = torch.arange(G, device=DEV) * RT + e * G * RT + pos
+            assert np.array_equal(h(out.scales[gi]), scales[:G])
