@@ -73,14 +73,30 @@ __global__ __launch_bounds__(1024) void dispatch_copy(const u32x4* __restrict__ 
 
 // P = 16-channel pairs per row (H / 16); a group of 128 channels is 8
 // pairs = 8 consecutive lanes, reduced with DPP.
+// Work-groups are dealt to the kXcds dies round-robin (block b on die
+// b % kXcds).  xcd_run maps block b to item (b % kXcds) * per + b / kXcds,
+// per = ceil(n / kXcds): each die walks a contiguous run of items in order.
+// A grid of kXcds * per blocks covers every item once (items >= n exit).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_run(int b, int n) {
+  const int per = (n + kXcds - 1) / kXcds;
+  return (b % kXcds) * per + b / kXcds;
+}
+
 template <int NP, int Q, bool LL>
 __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ send_pos,
                                                      u32x4* __restrict__ codes,
                                                      void* __restrict__ scales, int P, int K,
-                                                     int64_t cap, int G, int RT, int32_t* err) {
+                                                     int64_t cap, int G, int RT, int n_tok,
+                                                     int32_t* err) {
   const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x;
+  // low-latency: die blockIdx.x % kXcds takes a contiguous run of tokens, so
+  // consecutive slots of an expert (consecutive tokens) are stored from one
+  // L2 and their 4-byte column-major scales merge into whole lines there
+  const int tok = LL ? xcd_run(blockIdx.x, n_tok) : blockIdx.x;
+  if (tok >= n_tok) return;
   const int base = uniform(threadIdx.x >> 6) * kWave * NP;
   const u32x4* src = x + (int64_t)tok * (2 * (int64_t)P);
   u32x4 lo[NP], hi[NP];
@@ -196,9 +212,11 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
   const int N = a.g.R * a.g.T;
   // normal mode: rows also index the staging buffer, so they stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
-  hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL>), dim3(N), dim3(kWave * waves), 0, st,
+  const int blocks = LL ? kXcds * ((N + kXcds - 1) / kXcds) : N;
+  hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL>), dim3(blocks), dim3(kWave * waves), 0, st,
                      (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
-                     LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, a.err);
+                     LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
+                     a.err);
   if (!LL) {
     // 64 rows per tile, fewer for wide rows (the tile lives in LDS)
     const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;

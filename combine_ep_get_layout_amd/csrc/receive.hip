@@ -140,11 +140,22 @@ __global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
   for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
 }
 
-// Unpack: blockIdx.x = s * R + d; wavefront w takes local experts w, w + waves, ...
+// Unpack: one block per (s, d); wavefront w takes local experts w, w +
+// waves, ...  XCD-aware order: workgroups are dealt to the chip's
+// kXcds dies round-robin, so block b runs on die b % kXcds.  Destination d
+// is given die d % kXcds, and its messages follow in source order on that
+// die: the slots of an expert from consecutive sources are adjacent, and
+// their column-major scale stores (4 bytes each, one cache line per
+// (expert, group) column run) meet in the same L2 instead of being written
+// back as partial lines from eight L2s.
+constexpr int kXcds = 8;
+
 __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   const Geometry& g = a.g;
   const int R = g.R, L = g.L, E = g.E, K = g.K, H = g.H, G = g.G, T = g.T;
-  const int s = blockIdx.x / R, d = blockIdx.x % R;
+  const int x = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int d = x + kXcds * (rest / R), s = rest % R;
+  if (d >= R) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int64_t rt = (int64_t)R * T;
   // recv_count of d's experts: written once, by the block of source 0
@@ -256,7 +267,8 @@ hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st) {
   const int R = a.g.R;
   int waves = a.g.L < 16 ? a.g.L : 16;
-  hipLaunchKernelGGL(msg_unpack, dim3((unsigned)R * R), dim3(kWave * waves), 0, st, a);
+  const unsigned blocks = (unsigned)(kXcds * ((R + kXcds - 1) / kXcds) * R);  // (d, s) pairs
+  hipLaunchKernelGGL(msg_unpack, dim3(blocks), dim3(kWave * waves), 0, st, a);
   return hipGetLastError();
 }
 
