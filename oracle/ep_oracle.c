@@ -123,6 +123,20 @@ static int64_t roundup64(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 int64_t orc_recv_rows(const orc_problem* p, const int32_t* topk) {
   const int R = p->R, T = p->T, E = p->E, K = p->K;
   if (p->mode == ORC_MODE_LL) return (int64_t)E * R * T;
+  if (p->mode == ORC_MODE_RANK) { /* one row per (token, destination rank) */
+    const int L = E / R;
+    int64_t total = 0;
+    uint8_t* hit = (uint8_t*)malloc((size_t)(R > 0 ? R : 1));
+    for (int64_t tok = 0; tok < (int64_t)R * T; ++tok) {
+      memset(hit, 0, (size_t)R);
+      for (int k = 0; k < K; ++k) {
+        int32_t e = topk[tok * K + k];
+        if (e >= 0 && e < E && !hit[e / L]) { hit[e / L] = 1; ++total; }
+      }
+    }
+    free(hit);
+    return total;
+  }
   if (p->mode != ORC_MODE_NORMAL) return 0;
   int64_t* n = (int64_t*)calloc((size_t)E, sizeof(int64_t));
   for (int64_t i = 0; i < (int64_t)R * T * K; ++i) {
@@ -154,6 +168,13 @@ int64_t orc_recv_rows(const orc_problem* p, const int32_t* topk) {
  *  - send_head[s][t][d]: index of token t among the tokens s sends to
  *    rank d (in token order), -1 when t is not sent to d.
  *  - recv_src_idx[row] = s * T + t for every filled row, -1 elsewhere.
+ *  - Rank-major mode ([DEEP] sec. 2.3, the V1 receive buffer): rank d
+ *    receives each token with an expert on d once; its partition is ordered
+ *    by source rank (segment of s starts at rank_prefix[s-1][d], the
+ *    exclusive prefix) and then by the token's index in the (s, d) stream
+ *    (send_head); partitions are packed back to back.  send_pos[s][t][k]
+ *    is the row of token t on the rank of expert k (the same row for every
+ *    k on that rank).
  * Entries equal to -1 mean "no expert" and are skipped (reading: the
  * pages never state the index type or a masked value; int32 with -1 as
  * masked is the plain reading).  Out-of-range entries set an error bit and
@@ -206,7 +227,16 @@ int orc_layout(const orc_problem* p, const int32_t* topk, int32_t* cnt_rank,
   }
 
   /* segment starts */
-  if (p->mode == ORC_MODE_LL) {
+  if (p->mode == ORC_MODE_RANK) {
+    int32_t base = 0;
+    for (int d = 0; d < R; ++d) {
+      row_base[d] = base;
+      rows[d] = rank_prefix[(R - 1) * R + d];
+      for (int l = 0; l < L; ++l) expert_start[d * L + l] = base;
+      base += rows[d];
+    }
+    row_base[R] = base;
+  } else if (p->mode == ORC_MODE_LL) {
     for (int e = 0; e < E; ++e) expert_start[e] = e * R * T;
     for (int d = 0; d < R; ++d) {
       rows[d] = L * R * T;
@@ -233,6 +263,37 @@ int orc_layout(const orc_problem* p, const int32_t* topk, int32_t* cnt_rank,
   if (recv_src_idx != NULL) {
     if (p->mode != ORC_MODE_MSG && recv_cap < nrows) err |= ORC_ERR_CAPACITY;
     for (int64_t i = 0; i < recv_cap; ++i) recv_src_idx[i] = -1;
+  }
+
+  if (p->mode == ORC_MODE_RANK) {
+    /* rank-level slots: the stream index of the token, after the tokens of
+     * earlier sources */
+    int32_t* head = (int32_t*)malloc(sizeof(int32_t) * (R > 0 ? R : 1));
+    for (int s = 0; s < R; ++s) {
+      for (int d = 0; d < R; ++d) head[d] = 0;
+      for (int t = 0; t < T; ++t) {
+        for (int d = 0; d < R; ++d) {
+          int64_t hi = ((int64_t)s * T + t) * R + d;
+          int32_t v = in_rank[hi] ? head[d]++ : -1;
+          if (send_head != NULL) send_head[hi] = v;
+          if (v < 0) continue;
+          int32_t row = row_base[d] + (rank_prefix[s * R + d] - cnt_rank[s * R + d]) + v;
+          if (recv_src_idx != NULL && row < recv_cap) recv_src_idx[row] = s * T + t;
+        }
+        for (int k = 0; k < K; ++k) {
+          int64_t i = ((int64_t)s * T + t) * K + k;
+          int32_t e = topk[i], row = -1;
+          if (e >= 0 && e < E) {
+            int d = e / L;
+            row = row_base[d] + (rank_prefix[s * R + d] - cnt_rank[s * R + d]) +
+                  (head[d] - 1); /* this token was the last one counted on d */
+          }
+          if (send_pos != NULL) send_pos[i] = row;
+        }
+      }
+    }
+    free(head);
+    return err;
   }
 
   /* expert-level slots: one running counter per expert across all sources */
@@ -311,6 +372,28 @@ static void quantise_token(const orc_problem* p, const uint16_t* xrow, uint8_t* 
   }
 }
 
+/* Rank-major receive metadata (see the header). */
+int orc_rank_topk(const orc_problem* p, const int32_t* topk, const float* w,
+                  const int32_t* send_pos, int64_t cap, int32_t* recv_topk_idx,
+                  float* recv_topk_weights) {
+  const int R = p->R, T = p->T, E = p->E, K = p->K, L = E / R;
+  int err = 0;
+  for (int64_t tok = 0; tok < (int64_t)R * T; ++tok)
+    for (int k = 0; k < K; ++k) {
+      int32_t row = send_pos[tok * K + k];
+      if (row < 0) continue;
+      if (row >= cap) { err |= ORC_ERR_CAPACITY; continue; }
+      int d = topk[tok * K + k] / L;
+      for (int k2 = 0; k2 < K; ++k2) {
+        int32_t e = topk[tok * K + k2];
+        int on_d = e >= 0 && e < E && e / L == d;
+        recv_topk_idx[(int64_t)row * K + k2] = on_d ? e - d * L : -1;
+        recv_topk_weights[(int64_t)row * K + k2] = on_d ? w[tok * K + k2] : 0.0f;
+      }
+    }
+  return err;
+}
+
 /* Every routed (token, expert) entry copies the token to its slot row:
  * recv[send_pos[s][t][k]] = x[s][t] (bf16), or the token's FP8 codes plus
  * one scale per 128-channel group. */
@@ -330,6 +413,11 @@ int orc_dispatch(const orc_problem* p, const uint16_t* x, const int32_t* topk,
         (void)topk;
         int32_t row = send_pos[i];
         if (row < 0) continue;
+        if (p->mode == ORC_MODE_RANK) { /* one row per destination rank */
+          int seen = 0;
+          for (int k2 = 0; k2 < k; ++k2) seen |= send_pos[i - k + k2] == row;
+          if (seen) continue;
+        }
         if (row >= cap) { err |= ORC_ERR_CAPACITY; continue; }
         if (p->quant == ORC_Q_NONE) {
           memcpy((uint16_t*)recv + (int64_t)row * H, xrow, sizeof(uint16_t) * H);
@@ -392,8 +480,19 @@ int orc_combine(const orc_problem* p, const uint16_t* y, int64_t y_rows, const f
     for (int k = 0; k < K; ++k) {
       int32_t row = send_pos[tok * K + k];
       if (row < 0) continue;
+      double wk;
+      if (p->mode == ORC_MODE_RANK) {
+        /* rank-major: the token's rows on its destination ranks, each once,
+         * unweighted (the expert stage on rank d already applied the
+         * weights of d's experts) */
+        int seen = 0;
+        for (int k2 = 0; k2 < k; ++k2) seen |= send_pos[tok * K + k2] == row;
+        if (seen) continue;
+        wk = 1.0;
+      } else {
+        wk = (double)w[tok * K + k];
+      }
       if (row >= y_rows) { err |= ORC_ERR_CAPACITY; continue; }
-      double wk = (double)w[tok * K + k];
       const uint16_t* yrow = y + (int64_t)row * H;
       for (int c = 0; c < H; ++c) acc[c] += wk * orc_bf16_to_double(yrow[c]);
     }

@@ -49,6 +49,7 @@ extern "C" {
 #define ORC_MODE_NORMAL 0 /* contiguous, expert-major per destination rank   */
 #define ORC_MODE_LL 1     /* packed masked [E][R*T] rows                       */
 #define ORC_MODE_MSG 2    /* one message per (source, destination) rank pair   */
+#define ORC_MODE_RANK 3   /* rank-major: one row per (token, destination rank) */
 
 /* payload quantisation */
 #define ORC_Q_NONE 0      /* bf16 rows                                        */
@@ -97,6 +98,15 @@ int orc_layout(const orc_problem* p, const int32_t* topk /*[R][T][K]*/,
                int32_t* rows /*[R]*/, int32_t* row_base /*[R+1]*/,
                int32_t* send_pos /*[R][T][K]*/, int32_t* send_head /*[R][T][R]*/,
                int32_t* recv_src_idx /*[cap]*/, int64_t recv_cap);
+
+/* ---- rank-major receive metadata ------------------------------------ */
+/* For every row of the rank-major layout (mode ORC_MODE_RANK), the token's
+ * top-k as the destination rank d sees it: recv_topk_idx[row][k] = e - d*L
+ * when expert e = topk[s][t][k] lives on d, else -1; recv_topk_weights
+ * [row][k] = w[s][t][k] when it does, else 0.                             */
+int orc_rank_topk(const orc_problem* p, const int32_t* topk, const float* w,
+                  const int32_t* send_pos, int64_t cap, int32_t* recv_topk_idx /*[cap][K]*/,
+                  float* recv_topk_weights /*[cap][K]*/);
 
 /* ---- dispatch (normal / LL) ----------------------------------------- */
 /* recv: bf16 rows [cap][H] (quant NONE) or e4m3 codes [cap][H] (FP8).

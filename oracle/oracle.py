@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
 _LIB = os.path.join(_HERE, "libep_oracle.so")
 
-MODE_NORMAL, MODE_LL, MODE_MSG = 0, 1, 2
+MODE_NORMAL, MODE_LL, MODE_MSG, MODE_RANK = 0, 1, 2, 3
 Q_NONE, Q_FP8_F32, Q_FP8_UE8M0 = 0, 1, 2
 ERR_TOPK_RANGE, ERR_LL_OVERFLOW, ERR_CAPACITY, ERR_MESSAGE = 1, 2, 4, 8
 
@@ -84,6 +84,8 @@ def lib():
         _lib.orc_msg_body_bytes.restype = i64
         _lib.orc_messages.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
         _lib.orc_messages.restype = ctypes.c_int
+        _lib.orc_rank_topk.argtypes = [P, vp, vp, vp, i64, vp, vp]
+        _lib.orc_rank_topk.restype = ctypes.c_int
         _lib.orc_messages_execute.argtypes = [P, vp, i64, vp, vp, i64, vp, i64]
         _lib.orc_messages_execute.restype = ctypes.c_int
         _lib.orc_messages_unpack.argtypes = [P, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -201,6 +203,19 @@ def layout(p: Problem, topk: np.ndarray, recv_cap: int | None = None) -> Layout:
     )
     o["recv_src_idx"] = o["recv_src_idx"][:recv_cap]
     return Layout(err=err, **o)
+
+
+def rank_topk(p: Problem, topk: np.ndarray, w: np.ndarray, send_pos: np.ndarray, cap: int):
+    """Rank-major receive metadata: (err, recv_topk_idx [cap][K] (-1 fill),
+    recv_topk_weights [cap][K] (0 fill))."""
+    K = p.K
+    idx = np.full((max(cap, 1), K), -1, np.int32)
+    wts = np.zeros((max(cap, 1), K), np.float32)
+    err = lib().orc_rank_topk(ctypes.byref(p.c()), _ptr(np.ascontiguousarray(topk, np.int32)),
+                              _ptr(np.ascontiguousarray(w, np.float32)),
+                              _ptr(np.ascontiguousarray(send_pos, np.int32)), cap, _ptr(idx),
+                              _ptr(wts))
+    return err, idx[:cap], wts[:cap]
 
 
 # ---------------------------------------------------------------- dispatch
