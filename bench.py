@@ -39,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-DEFAULT_WORKLOADS = ["normal_prefill", "ll_decode", "fp8_train", "messages"]
+DEFAULT_WORKLOADS = ["normal_prefill", "ll_decode", "fp8_train", "messages", "rank_prefill"]
 
 
 def log(*a):
@@ -57,16 +57,20 @@ def layout_bytes(w, rows_written):
     return b
 
 
-def dispatch_bytes(w):
+def dispatch_bytes(w, rows=None):
     R, T, H, K, G = w.R, w.T, w.H, w.K, w.G
     N, M = R * T, R * T * K
     row = {0: 2 * H, 1: H + 4 * G, 2: H + G}[w.quant]
+    if w.mode == 3:  # rank-major: one row per (token, rank), plus its top-k ids and weights
+        return 2 * H * N + rows * (row + 8 * K) + 4 * M + 8 * M
     return 2 * H * N + row * M + 4 * M
 
 
-def combine_bytes(w):
+def combine_bytes(w, rows=None):
     R, T, H, K = w.R, w.T, w.H, w.K
     N, M = R * T, R * T * K
+    if w.mode == 3:  # rank-major: each distinct row once, unweighted
+        return 2 * H * rows + 2 * H * N + 4 * M
     return 2 * H * M + 2 * H * N + 8 * M
 
 
@@ -145,7 +149,7 @@ class Runner:
                             "execute": "msg_exec_puts", "unpack": "msg_unpack"}
             self.extra = {"messages": n_msg, "descriptors": nd, "message_bytes": msg_bytes}
             return
-        if w.mode == ep.MODE_NORMAL:
+        if w.mode in (ep.MODE_NORMAL, ep.MODE_RANK_MAJOR):
             self.rows = int(self.lay.row_base[-1].item())  # untimed read-back of the receive size
             filled = self.rows
         else:
@@ -160,8 +164,8 @@ class Runner:
             self.y = torch.empty((self.rows, w.H), dtype=torch.bfloat16, device=dev)
             self.y.normal_()
         self.out = torch.empty((w.R, w.T, w.H), dtype=torch.bfloat16, device=dev)
-        self.bytes = {"layout": layout_bytes(w, filled), "dispatch": dispatch_bytes(w),
-                      "combine": combine_bytes(w)}
+        self.bytes = {"layout": layout_bytes(w, filled), "dispatch": dispatch_bytes(w, self.rows),
+                      "combine": combine_bytes(w, self.rows)}
         self.kernels = {"dispatch": "dispatch_copy" if w.quant == 0 else "dispatch_fp8",
                         "combine": "combine_rows"}
         self.extra = {}
@@ -182,9 +186,16 @@ class Runner:
                                                             self.lay.num_tokens_per_expert,
                                                             *self.unp, self.err)))
         else:
-            ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
-                                                       ws=self.ws)))
-            ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, self.wt, self.out)))
+            if self.w.mode == ep.MODE_RANK_MAJOR:  # rows plus their top-k metadata
+                ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
+                                                           topk_idx=self.topk,
+                                                           topk_weights=self.wt, ws=self.ws)))
+                ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, None, self.out)))
+            else:
+                ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
+                                                           ws=self.ws)))
+                ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, self.wt,
+                                                         self.out)))
         self._phases = ph
         return ph
 
@@ -237,7 +248,7 @@ class Runner:
         dom = max(self.kernels, key=lambda k: mean_ph[k])
         kname = self.kernels[dom]
         ach = self.bytes[dom] / (mean_ph[dom] * 1e-3) / 1e9
-        mode = {0: "contiguous", 1: "packed-masked", 2: "messages"}[w.mode]
+        mode = {0: "contiguous", 1: "packed-masked", 2: "messages", 3: "rank-major"}[w.mode]
         payload = {0: "bf16", 1: "fp8-e4m3 fp32 scales", 2: "fp8-e4m3 ue8m0 scales"}[w.quant]
         res = {
             "workload": f"{w.name} R{w.R} T{w.T} H{w.H} E{w.E} K{w.K} "

@@ -21,7 +21,21 @@ namespace ep {
 // fused multiply-adds (8 rows per group for one vector per lane, fewer for
 // wider pieces so the loads stay in registers).
 
-template <int NV>
+// Rank-major mode: a token's entries on one destination rank share a row;
+// bit k is set for the first entry of each distinct row (lanes k < K hold
+// the rows).
+__device__ __forceinline__ uint64_t first_rows(int myrow, int K) {
+  bool dup = false;
+  for (int k2 = 0; k2 < K; ++k2) {
+    const int r2 = __builtin_amdgcn_readlane(myrow, k2);
+    dup |= k2 < lane_id() && r2 == myrow;
+  }
+  return __ballot(lane_id() < K && myrow >= 0 && !dup);
+}
+
+// RM (rank-major): sum the token's distinct rows with weight 1 and skip the
+// loads of repeated rows.
+template <int NV, bool RM>
 __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y,
                                                      const int32_t* __restrict__ send_pos,
                                                      const float* __restrict__ w,
@@ -31,7 +45,8 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
   const int tok = blockIdx.x;
   const int base = uniform(threadIdx.x >> 6) * kWave * NV;
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
-  const float myw = lane < K ? w[(int64_t)tok * K + lane] : 0.0f;
+  const float myw = RM ? 1.0f : (lane < K ? w[(int64_t)tok * K + lane] : 0.0f);
+  const uint64_t keep = RM ? first_rows(myrow, K) : ~0ull;
   constexpr int kGroup = NV == 1 ? 8 : (NV == 2 ? 4 : 2);
   float acc[NV][8];
 #pragma unroll
@@ -44,20 +59,27 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
     for (int kk = 0; kk < kGroup; ++kk) {
       const int k = k0 + kk;
       int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
+      if (RM && !((keep >> k) & 1)) row = -1;
       if (row >= y_rows) {
         if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
         row = -1;
       }
       const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;  // row 0 stands in, weight 0
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
+      for (int i = 0; i < NV; ++i) {
+        if (RM && row < 0) {  // rank-major: a repeated row is not read at all
+          v[kk][i] = u32x4{0u, 0u, 0u, 0u};
+          continue;
+        }
         v[kk][i] = y_rows > 0 ? __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1))
                               : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < kGroup; ++kk) {
       const int k = k0 + kk;
       if (k >= K) break;
+      if (RM && !((keep >> k) & 1)) continue;
       const int row = __builtin_amdgcn_readlane(myrow, k);
       if (row < 0 || row >= y_rows) continue;
       const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), k));
@@ -91,8 +113,13 @@ constexpr int kPipeK = 8;
 constexpr int kPipeTokens = 2;
 constexpr int64_t kPipeMinTokens = 8192;
 
-__device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, int K, int j,
-                                           int V, int64_t y_rows, u32x4 (&v)[kPipeK]) {
+// Loads of one token's (up to kPipeK) rows, one vector per lane.  Rows the
+// mask drops (masked entries, rank-major repeats) are not read in rank-major
+// mode; otherwise row 0 stands in, with weight 0.
+template <bool RM>
+__device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, uint64_t keep,
+                                           int K, int j, int V, int64_t y_rows,
+                                           u32x4 (&v)[kPipeK]) {
   if (y_rows == 0) {  // nothing to read; every entry is skipped
 #pragma unroll
     for (int k = 0; k < kPipeK; ++k) v[k] = u32x4{0u, 0u, 0u, 0u};
@@ -101,11 +128,17 @@ __device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myro
 #pragma unroll
   for (int k = 0; k < kPipeK; ++k) {
     int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
+    if (RM && !((keep >> k) & 1)) row = -1;
     if (row >= y_rows) row = -1;
+    if (RM && row < 0) {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
     v[k] = __builtin_nontemporal_load(y + (int64_t)(row < 0 ? 0 : row) * V + min(j, V - 1));
   }
 }
 
+template <bool RM>
 __global__ __launch_bounds__(1024) void combine_rows_pipe(const u32x4* __restrict__ y,
                                                           const int32_t* __restrict__ send_pos,
                                                           const float* __restrict__ w,
@@ -116,18 +149,21 @@ __global__ __launch_bounds__(1024) void combine_rows_pipe(const u32x4* __restric
   const int j = uniform(threadIdx.x >> 6) * kWave + lane;
   const int tok0 = blockIdx.x * kPipeTokens;
   int myrow = lane < K ? send_pos[(int64_t)tok0 * K + lane] : -1;
+  uint64_t keep = RM ? first_rows(myrow, K) : ~0ull;
   u32x4 a[kPipeK];
-  load_rows8(y, myrow, K, j, V, y_rows, a);
+  load_rows8<RM>(y, myrow, keep, K, j, V, y_rows, a);
   for (int r = 0; r < kPipeTokens; ++r) {
     const int tok = tok0 + r;
     if (tok >= n_tok) break;
-    const float myw = lane < K ? w[(int64_t)tok * K + lane] : 0.0f;
+    const float myw = RM ? 1.0f : (lane < K ? w[(int64_t)tok * K + lane] : 0.0f);
     u32x4 b[kPipeK];
     int nextrow = -1;
+    uint64_t nextkeep = 0;
     const bool more = r + 1 < kPipeTokens && tok + 1 < n_tok;
     if (more) {
       nextrow = lane < K ? send_pos[(int64_t)(tok + 1) * K + lane] : -1;
-      load_rows8(y, nextrow, K, j, V, y_rows, b);
+      nextkeep = RM ? first_rows(nextrow, K) : ~0ull;
+      load_rows8<RM>(y, nextrow, nextkeep, K, j, V, y_rows, b);
     }
     float acc[8];
 #pragma unroll
@@ -135,6 +171,7 @@ __global__ __launch_bounds__(1024) void combine_rows_pipe(const u32x4* __restric
 #pragma unroll
     for (int k = 0; k < kPipeK; ++k) {
       if (k >= K) break;
+      if (RM && !((keep >> k) & 1)) continue;
       const int row = __builtin_amdgcn_readlane(myrow, k);
       if (row < 0) continue;
       if (row >= y_rows) {
@@ -159,15 +196,27 @@ __global__ __launch_bounds__(1024) void combine_rows_pipe(const u32x4* __restric
 #pragma unroll
       for (int k = 0; k < kPipeK; ++k) a[k] = b[k];
       myrow = nextrow;
+      keep = nextkeep;
     }
   }
 }
 
-template <int NV>
+template <int NV, bool RM>
 static void launch_nv(const CombineArgs& a, int V, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
-  hipLaunchKernelGGL(combine_rows<NV>, dim3(N), dim3(kWave * waves), 0, st, (const u32x4*)a.y,
-                     a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, a.y_rows, a.err);
+  hipLaunchKernelGGL((combine_rows<NV, RM>), dim3(N), dim3(kWave * waves), 0, st,
+                     (const u32x4*)a.y, a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, a.y_rows,
+                     a.err);
+}
+
+template <bool RM>
+static void launch_rows(const CombineArgs& a, int nv, int V, int waves, hipStream_t st) {
+  switch (nv) {
+    case 1: launch_nv<1, RM>(a, V, waves, st); break;
+    case 2: launch_nv<2, RM>(a, V, waves, st); break;
+    case 3: launch_nv<3, RM>(a, V, waves, st); break;
+    default: launch_nv<4, RM>(a, V, waves, st); break;  // hidden <= 32768: nv <= 4
+  }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
@@ -180,17 +229,17 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   // two tokens per block only when there are enough blocks to fill the chip
   if (nv == 1 && a.g.K <= kPipeK && N >= kPipeMinTokens) {
     const int n = (int)N;
-    hipLaunchKernelGGL(combine_rows_pipe, dim3((n + kPipeTokens - 1) / kPipeTokens),
-                       dim3(kWave * waves), 0, st, (const u32x4*)a.y, a.send_pos, a.w,
-                       (u32x4*)a.out, V, a.g.K, n, a.y_rows, a.err);
+    const dim3 grid((n + kPipeTokens - 1) / kPipeTokens), block(kWave * waves);
+    if (a.rank_major)
+      hipLaunchKernelGGL(combine_rows_pipe<true>, grid, block, 0, st, (const u32x4*)a.y,
+                         a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, n, a.y_rows, a.err);
+    else
+      hipLaunchKernelGGL(combine_rows_pipe<false>, grid, block, 0, st, (const u32x4*)a.y,
+                         a.send_pos, a.w, (u32x4*)a.out, V, a.g.K, n, a.y_rows, a.err);
     return hipGetLastError();
   }
-  switch (nv) {
-    case 1: launch_nv<1>(a, V, waves, st); break;
-    case 2: launch_nv<2>(a, V, waves, st); break;
-    case 3: launch_nv<3>(a, V, waves, st); break;
-    default: launch_nv<4>(a, V, waves, st); break;  // hidden <= 32768: nv <= 4
-  }
+  if (a.rank_major) launch_rows<true>(a, nv, V, waves, st);
+  else launch_rows<false>(a, nv, V, waves, st);
   return hipGetLastError();
 }
 

@@ -42,11 +42,43 @@ inline RowSplit row_split(int vectors, int prefer_nv) {
   return r;
 }
 
-template <int NV>
+// Rank-major mode: the token's rows on its destination ranks.  Lanes k < K
+// hold send_pos of entry k; bit k of the result is set when entry k is the
+// first entry with that row (one row per destination rank).
+__device__ __forceinline__ uint64_t first_of_rows(int myrow, int K) {
+  bool dup = false;
+  for (int k2 = 0; k2 < K; ++k2) {
+    const int r2 = __builtin_amdgcn_readlane(myrow, k2);
+    dup |= k2 < lane_id() && r2 == myrow;
+  }
+  return __ballot(lane_id() < K && myrow >= 0 && !dup);
+}
+
+// Rank-major per-row metadata.  Lane k (< K) writes entry k of the row as
+// rank d sees it: the local id of expert e_k when it lives on d, else -1,
+// and its weight, else 0.
+struct RowMeta {
+  const int32_t* topk;
+  const float* w;
+  int32_t* idx;  // [capacity][K] or NULL
+  float* wts;    // [capacity][K] or NULL
+  int L, E;
+};
+
+__device__ __forceinline__ void write_row_meta(const RowMeta& m, int K, int64_t row, int d,
+                                               int myid, float myw) {
+  const int lane = lane_id();
+  if (lane >= K) return;
+  const bool on = myid >= 0 && myid < m.E && myid / m.L == d;
+  if (m.idx) m.idx[row * K + lane] = on ? myid - d * m.L : -1;
+  if (m.wts) m.wts[row * K + lane] = on ? myw : 0.0f;
+}
+
+template <int NV, bool RM>
 __global__ __launch_bounds__(1024) void dispatch_copy(const u32x4* __restrict__ x,
                                                       const int32_t* __restrict__ send_pos,
                                                       u32x4* __restrict__ recv, int V, int K,
-                                                      int64_t cap, int32_t* err) {
+                                                      int64_t cap, int32_t* err, RowMeta meta) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x;
   const int base = uniform(threadIdx.x >> 6) * kWave * NV;
@@ -55,13 +87,21 @@ __global__ __launch_bounds__(1024) void dispatch_copy(const u32x4* __restrict__ 
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = src[min(base + lane + kWave * i, V - 1)];  // in bounds
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
+  // rank-major: each destination row once; the first wave writes its metadata
+  const uint64_t keep = RM ? first_of_rows(myrow, K) : ~0ull;
+  const bool meta_wave = RM && base == 0 && (meta.idx || meta.wts);
+  const int myid = meta_wave && lane < K ? meta.topk[(int64_t)tok * K + lane] : -1;
+  const float myw = meta_wave && meta.wts && lane < K ? meta.w[(int64_t)tok * K + lane] : 0.0f;
   for (int k = 0; k < K; ++k) {
+    if (RM && !((keep >> k) & 1)) continue;
     const int row = __builtin_amdgcn_readlane(myrow, k);
     if (row < 0) continue;
     if (row >= cap) {
       if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
       continue;
     }
+    if (meta_wave)
+      write_row_meta(meta, K, row, __builtin_amdgcn_readlane(myid, k) / meta.L, myid, myw);
     u32x4* dst = recv + (int64_t)row * V;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -84,13 +124,13 @@ __device__ __forceinline__ int xcd_run(int b, int n) {
   return (b % kXcds) * per + b / kXcds;
 }
 
-template <int NP, int Q, bool LL>
+template <int NP, int Q, bool LL, bool RM>
 __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ send_pos,
                                                      u32x4* __restrict__ codes,
                                                      void* __restrict__ scales, int P, int K,
                                                      int64_t cap, int G, int RT, int n_tok,
-                                                     int32_t* err) {
+                                                     int32_t* err, RowMeta meta) {
   const int lane = threadIdx.x & 63;
   // low-latency: die blockIdx.x % kXcds takes a contiguous run of tokens, so
   // consecutive slots of an expert (consecutive tokens) are stored from one
@@ -107,13 +147,21 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
 #pragma unroll
   for (int i = 0; i < NP; ++i) quantise_pair<Q>(lo[i], hi[i], cv[i], scf[i], sce[i]);
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
+  // rank-major: each destination row once; the first wave writes its metadata
+  const uint64_t keep = RM ? first_of_rows(myrow, K) : ~0ull;
+  const bool meta_wave = RM && base == 0 && (meta.idx || meta.wts);
+  const int myid = meta_wave && lane < K ? meta.topk[(int64_t)tok * K + lane] : -1;
+  const float myw = meta_wave && meta.wts && lane < K ? meta.w[(int64_t)tok * K + lane] : 0.0f;
   for (int k = 0; k < K; ++k) {
+    if (RM && !((keep >> k) & 1)) continue;
     const int row = __builtin_amdgcn_readlane(myrow, k);
     if (row < 0) continue;
     if (row >= cap) {
       if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
       continue;
     }
+    if (meta_wave)
+      write_row_meta(meta, K, row, __builtin_amdgcn_readlane(myid, k) / meta.L, myid, myw);
     u32x4* dst = codes + (int64_t)row * P;
     int64_t sbase, sstride;
     if (LL) {  // column-major per expert, written in place
@@ -155,7 +203,7 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
                                                          const int32_t* row_base_end,
                                                          const int32_t* __restrict__ expert_start,
                                                          const int32_t* __restrict__ count,
-                                                         int E, int tile_rows) {
+                                                         int E, int tile_rows, int all_filled) {
   extern __shared__ uint32_t lds[];
   int* starts = (int*)lds;                  // E + 1
   int* filled = starts + E + 1;             // tile_rows
@@ -178,7 +226,9 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
   for (int r = threadIdx.x; r < tile_rows; r += blockDim.x) {
     const int64_t row = r0 + r;
     int ok = 0;
-    if (r < nrows) {
+    if (r < nrows && all_filled) {
+      ok = 1;  // rank-major: no padding rows
+    } else if (r < nrows) {
       int lo = 0, hi = E;  // last e with starts[e] <= row
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -200,23 +250,36 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
   }
 }
 
-template <int NV>
-static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t st) {
-  const int N = a.g.R * a.g.T;
-  hipLaunchKernelGGL(dispatch_copy<NV>, dim3(N), dim3(kWave * waves), 0, st, (const u32x4*)a.x,
-                     a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err);
+inline RowMeta row_meta(const DispatchArgs& a) {
+  RowMeta m;
+  m.topk = a.topk;
+  m.w = a.w;
+  m.idx = a.recv_topk_idx;
+  m.wts = a.recv_topk_weights;
+  m.L = a.g.L;
+  m.E = a.g.E;
+  return m;
 }
 
-template <int NP, int Q, bool LL>
+template <int NV, bool RM>
+static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t st) {
+  const int N = a.g.R * a.g.T;
+  hipLaunchKernelGGL((dispatch_copy<NV, RM>), dim3(N), dim3(kWave * waves), 0, st,
+                     (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
+                     row_meta(a));
+}
+
+template <int NP, int Q, bool LL, bool RM>
 static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
-  // normal mode: rows also index the staging buffer, so they stay below both
+  // normal and rank-major modes: rows also index the staging buffer, so they
+  // stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
   const int blocks = LL ? kXcds * ((N + kXcds - 1) / kXcds) : N;
-  hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL>), dim3(blocks), dim3(kWave * waves), 0, st,
+  hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, RM>), dim3(blocks), dim3(kWave * waves), 0, st,
                      (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
                      LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
-                     a.err);
+                     a.err, row_meta(a));
   if (!LL) {
     // 64 rows per tile, fewer for wide rows (the tile lives in LDS)
     const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;
@@ -229,27 +292,34 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
         hipLaunchKernelGGL(scales_to_columns<4>, dim3((unsigned)tiles), dim3(256), lds, st,
                            (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
                            a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
-                           tile_rows);
+                           tile_rows, RM ? 1 : 0);
       else
         hipLaunchKernelGGL(scales_to_columns<1>, dim3((unsigned)tiles), dim3(256), lds, st,
                            (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
                            a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
-                           tile_rows);
+                           tile_rows, RM ? 1 : 0);
     }
   }
 }
 
-template <int Q, bool LL>
+template <int Q, bool LL, bool RM>
 static void launch_fp8_q(const DispatchArgs& a, hipStream_t st) {
   const int P = a.g.H / 16;
   RowSplit rs = row_split(P, 1);
   if (rs.nv >= 3) rs = RowSplit{4, ((P + kWave * 4 - 1) / (kWave * 4) + 3) / 4 * 4};  // <= 8 waves
   switch (rs.nv) {
-    case 1: launch_fp8_np<1, Q, LL>(a, P, rs.waves, st); break;
-    case 2: launch_fp8_np<2, Q, LL>(a, P, rs.waves, st); break;
-    case 3: launch_fp8_np<3, Q, LL>(a, P, rs.waves, st); break;
-    default: launch_fp8_np<4, Q, LL>(a, P, rs.waves, st); break;  // hidden <= 32768
+    case 1: launch_fp8_np<1, Q, LL, RM>(a, P, rs.waves, st); break;
+    case 2: launch_fp8_np<2, Q, LL, RM>(a, P, rs.waves, st); break;
+    case 3: launch_fp8_np<3, Q, LL, RM>(a, P, rs.waves, st); break;
+    default: launch_fp8_np<4, Q, LL, RM>(a, P, rs.waves, st); break;  // hidden <= 32768
   }
+}
+
+template <int Q>
+static void launch_fp8_mode(const DispatchArgs& a, hipStream_t st) {
+  if (a.mode == EP_MODE_LOW_LATENCY) launch_fp8_q<Q, true, false>(a, st);
+  else if (a.rank_major) launch_fp8_q<Q, false, true>(a, st);
+  else launch_fp8_q<Q, false, false>(a, st);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
@@ -258,16 +328,12 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   if (a.quant == EP_QUANT_NONE) {
     const int V = a.g.H / 8;
     const RowSplit rs = row_split(V, 4);  // hidden <= 32768: nv = 4, <= 16 waves
-    launch_copy_nv<4>(a, V, rs.waves, st);
+    if (a.rank_major) launch_copy_nv<4, true>(a, V, rs.waves, st);
+    else launch_copy_nv<4, false>(a, V, rs.waves, st);
+  } else if (a.quant == EP_QUANT_FP8_F32) {
+    launch_fp8_mode<EP_QUANT_FP8_F32>(a, st);
   } else {
-    const bool ll = a.mode == EP_MODE_LOW_LATENCY;
-    if (a.quant == EP_QUANT_FP8_F32) {
-      if (ll) launch_fp8_q<EP_QUANT_FP8_F32, true>(a, st);
-      else launch_fp8_q<EP_QUANT_FP8_F32, false>(a, st);
-    } else {
-      if (ll) launch_fp8_q<EP_QUANT_FP8_UE8M0, true>(a, st);
-      else launch_fp8_q<EP_QUANT_FP8_UE8M0, false>(a, st);
-    }
+    launch_fp8_mode<EP_QUANT_FP8_UE8M0>(a, st);
   }
   return hipGetLastError();
 }

@@ -42,7 +42,7 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   const int R = p->num_ranks, T = p->num_tokens, H = p->hidden, E = p->num_experts,
             K = p->num_topk;
   if (p->reserved != 0) return EP_ERR_SHAPE;
-  if (p->mode < EP_MODE_NORMAL || p->mode > EP_MODE_MESSAGES) return EP_ERR_MODE;
+  if (p->mode < EP_MODE_NORMAL || p->mode > EP_MODE_RANK_MAJOR) return EP_ERR_MODE;
   if (p->quant < EP_QUANT_NONE || p->quant > EP_QUANT_FP8_UE8M0) return EP_ERR_MODE;
   if (R < 1 || R > 256 || T < 0 || K < 1 || K > 64) return EP_ERR_SHAPE;
   if (E < R || E > 2048 || E % R != 0) return EP_ERR_SHAPE;
@@ -74,7 +74,7 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   g->tb = tb;
   // small problems: one launch with a block per expert and per rank, each
   // reading every entry (16 entries per thread of a 1024-thread block)
-  g->direct = entries <= kDirectMaxEntries ? 1 : 0;
+  g->direct = entries <= kDirectMaxEntries && p->mode != EP_MODE_RANK_MAJOR ? 1 : 0;
   // fewer, longer chunks only when there are plenty of them
   const int64_t batches = (int64_t)R * ((T + tb - 1) / tb);
   int64_t per = (batches + kTargetChunks - 1) / kTargetChunks;
@@ -97,9 +97,12 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   g->off_msg = off;
   if (p->mode == EP_MODE_MESSAGES) off += up256(message_ws_bytes(R));
   g->off_stage = off;
-  if (p->mode == EP_MODE_NORMAL && p->quant != EP_QUANT_NONE) {
+  if ((p->mode == EP_MODE_NORMAL || p->mode == EP_MODE_RANK_MAJOR) &&
+      p->quant != EP_QUANT_NONE) {
     // row-major scale staging for the worst-case number of receive rows
-    const int64_t rows = entries + (int64_t)E * (p->expert_alignment - 1);
+    const int64_t rows = p->mode == EP_MODE_RANK_MAJOR
+                             ? (int64_t)R * T * (K < R ? K : R)
+                             : entries + (int64_t)E * (p->expert_alignment - 1);
     off += up256((size_t)rows * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
   }
   g->ws_bytes = off < 256 ? 256 : off;
@@ -118,6 +121,7 @@ int64_t ep_max_recv_rows(const ep_problem* p) {
   Geometry g;
   if (ep::make_geometry(p, &g) != EP_OK) return -1;
   if (p->mode == EP_MODE_LOW_LATENCY) return (int64_t)g.E * g.R * g.T;
+  if (p->mode == EP_MODE_RANK_MAJOR) return (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R);
   return (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
 }
 
@@ -208,7 +212,17 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
     if (recv->capacity < 0) return EP_ERR_CAPACITY;
     if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
       return EP_ERR_CAPACITY;
-    const bool staged = p->mode == EP_MODE_NORMAL && p->quant != EP_QUANT_NONE;
+    const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;
+    const bool staged =
+        (p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE;
+    if (rank_major && toks) {
+      // per-row metadata needs the routing (ids) and, for weights, the weights
+      if ((recv->topk_idx || recv->topk_weights) && !topk_idx) return EP_ERR_NULL;
+      if (recv->topk_weights && !topk_weights) return EP_ERR_NULL;
+      if (!aligned(recv->topk_idx, 4) || !aligned(recv->topk_weights, 4) ||
+          !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
+        return EP_ERR_ALIGN;
+    }
     if (staged && toks) {
       if (!workspace || !layout->expert_start || !layout->recv_tokens_per_expert ||
           !layout->row_base)
@@ -221,7 +235,13 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
     a.mode = p->mode;
     a.quant = p->quant;
     a.stage = staged ? (char*)workspace + g.off_stage : nullptr;
-    a.stage_rows = (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+    a.stage_rows = rank_major ? (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R)
+                              : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+    a.rank_major = rank_major;
+    a.topk = rank_major ? topk_idx : nullptr;
+    a.w = rank_major ? topk_weights : nullptr;
+    a.recv_topk_idx = rank_major ? recv->topk_idx : nullptr;
+    a.recv_topk_weights = rank_major ? recv->topk_weights : nullptr;
     a.expert_start = layout->expert_start;
     a.recv_per_expert = layout->recv_tokens_per_expert;
     a.row_base = layout->row_base;
@@ -349,7 +369,8 @@ int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y, 
   if (p->mode == EP_MODE_MESSAGES) return EP_ERR_MODE;
   const bool toks = (int64_t)g.R * g.T > 0;
   if (!layout || !layout->err) return EP_ERR_NULL;
-  if (toks && (!layout->send_pos || !topk_weights || !out || (!y && y_rows > 0)))
+  const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;  // unweighted: no weights read
+  if (toks && (!layout->send_pos || (!topk_weights && !rank_major) || !out || (!y && y_rows > 0)))
     return EP_ERR_NULL;
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) ||
       !aligned(layout->send_pos, 4) || !aligned(layout->err, 4))
@@ -360,7 +381,8 @@ int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y, 
   a.y = y;
   a.y_rows = y_rows;
   a.send_pos = layout->send_pos;
-  a.w = topk_weights;
+  a.w = rank_major ? nullptr : topk_weights;
+  a.rank_major = rank_major;
   a.out = out;
   a.err = layout->err;
   if (ep::launch_combine(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;

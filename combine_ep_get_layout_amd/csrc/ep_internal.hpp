@@ -71,6 +71,13 @@ struct DispatchArgs {
   const int32_t* expert_start;
   const int32_t* recv_per_expert;
   const int32_t* row_base;
+  // rank-major: one row per (token, destination rank); optional per-row
+  // top-k metadata from the routing and weights
+  bool rank_major;
+  const int32_t* topk;
+  const float* w;
+  int32_t* recv_topk_idx;
+  float* recv_topk_weights;
 };
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
@@ -80,7 +87,8 @@ struct CombineArgs {
   const uint16_t* y;
   int64_t y_rows;
   const int32_t* send_pos;
-  const float* w;
+  const float* w;          // NULL in rank-major mode
+  bool rank_major;         // sum the token's distinct rows, unweighted
   uint16_t* out;
   int32_t* err;
 };

@@ -201,6 +201,28 @@ __global__ __launch_bounds__(1024) void layout_scan(LayoutArgs a) {
 // finalize launch computes them itself from the per-expert receive counts
 // (an exclusive scan of the counts rounded up to expert_alignment; fixed
 // blocks of R*T rows in low-latency mode).
+// Rank-major mode: partition bases in rbase[0..R] (exclusive scan of the
+// rows each rank receives, the last row of the rank prefix matrix), and
+// start[e] = base of e's rank.
+__device__ void rank_bases(const LayoutArgs& a, int* start, int* rbase) {
+  const Geometry& g = a.g;
+  const int per = (g.R + blockDim.x - 1) / blockDim.x;
+  const int lo = min(g.R, (int)threadIdx.x * per), hi = min(g.R, lo + per);
+  int sum = 0;
+  for (int d = lo; d < hi; ++d) sum += a.rpm[(g.R - 1) * g.R + d];
+  int total;
+  int run = block_exclusive_scan(sum, &total);
+  for (int d = lo; d < hi; ++d) {
+    rbase[d] = run;
+    run += a.rpm[(g.R - 1) * g.R + d];
+  }
+  if (threadIdx.x == 0) rbase[g.R] = total;
+  __syncthreads();
+  for (int e = threadIdx.x; e < g.E; e += blockDim.x) start[e] = rbase[e / g.L];
+  if (threadIdx.x == 0) start[g.E] = total;
+  __syncthreads();
+}
+
 __device__ void segment_starts(const LayoutArgs& a, int* start) {
   const Geometry& g = a.g;
   if (a.mode == EP_MODE_LOW_LATENCY) {
@@ -236,14 +258,17 @@ struct FirstItems {
   int e, local, head;
 };
 
-__device__ void finalize_body(const LayoutArgs& a, const int* start, const int32_t* hist_e,
-                              const int32_t* hist_r, const FirstItems& pre) {
+__device__ void finalize_body(const LayoutArgs& a, const int* start, const int* rbase,
+                              const int32_t* hist_e, const int32_t* hist_r,
+                              const FirstItems& pre) {
   const Geometry& g = a.g;
+  const bool rank_major = a.mode == EP_MODE_RANK_MAJOR;
   if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e < g.E; e += blockDim.x) a.expert_start[e] = start[e];
     for (int d = threadIdx.x; d <= g.R; d += blockDim.x) {
-      a.row_base[d] = start[d * g.L];
-      if (d < g.R) a.rows[d] = start[(d + 1) * g.L] - start[d * g.L];
+      const int b0 = rank_major ? rbase[d] : start[d * g.L];
+      a.row_base[d] = b0;
+      if (d < g.R) a.rows[d] = (rank_major ? rbase[d + 1] : start[(d + 1) * g.L]) - b0;
     }
   }
   if (a.mode == EP_MODE_NORMAL && a.recv_src_idx && a.align > 1) {
@@ -254,7 +279,8 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32
     }
   }
   const int64_t n_ent = (int64_t)g.R * g.T * g.K;
-  const int64_t n_head = a.send_head ? (int64_t)g.R * g.T * g.R : 0;
+  // rank-major rows come from the stream indices, needed even without send_head
+  const int64_t n_head = (a.send_head || rank_major) ? (int64_t)g.R * g.T * g.R : 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int rt = g.R * g.T;
   // one index walks both the (token, k) entries and the (token, rank) heads,
@@ -272,14 +298,22 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32
       if (local >= 0) {
         const int64_t st = i / g.K;  // s * T + t
         const int s = (int)(st / g.T), t = (int)(st % g.T);
-        const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
-        if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
-          set_err(a.err, EP_DEVERR_LL_OVERFLOW);
+        if (rank_major) {
+          // the token's row on the expert's rank: its stream index there
+          const int d = e / g.L;
+          const int64_t hi = st * g.R + d;
+          const int head = a.local_r[hi] + hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
+          row = rbase[d] + a.rpm[s * g.R + d] - a.cnt_rank[s * g.R + d] + head;
         } else {
-          row = start[e] + pos;
-          if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
-            if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
-            else set_err(a.err, EP_DEVERR_CAPACITY);
+          const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
+          if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
+            set_err(a.err, EP_DEVERR_LL_OVERFLOW);
+          } else {
+            row = start[e] + pos;
+            if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
+              if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
+              else set_err(a.err, EP_DEVERR_CAPACITY);
+            }
           }
         }
       }
@@ -291,8 +325,13 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int32
         const int d = (int)(i % g.R);
         const int s = (int)(st / g.T), t = (int)(st % g.T);
         v += hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
+        if (rank_major && a.recv_src_idx) {
+          const int row = rbase[d] + a.rpm[s * g.R + d] - a.cnt_rank[s * g.R + d] + v;
+          if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
+          else set_err(a.err, EP_DEVERR_CAPACITY);
+        }
       }
-      a.send_head[i] = v;
+      if (a.send_head) a.send_head[i] = v;
     }
   }
 }
@@ -307,15 +346,18 @@ __device__ FirstItems first_items(const LayoutArgs& a) {
     f.e = a.topk[i0];
     f.local = a.local_e[i0];
   }
-  if (a.send_head && i0 < (int64_t)g.R * g.T * g.R) f.head = a.local_r[i0];
+  if ((a.send_head || a.mode == EP_MODE_RANK_MAJOR) && i0 < (int64_t)g.R * g.T * g.R)
+    f.head = a.local_r[i0];
   return f;
 }
 
 __global__ __launch_bounds__(256) void layout_finalize(LayoutArgs a) {
   __shared__ int start[2049];
+  __shared__ int rbase[257];
   const FirstItems pre = first_items(a);
-  segment_starts(a, start);
-  finalize_body(a, start, a.hist_e, a.hist_r, pre);
+  if (a.mode == EP_MODE_RANK_MAJOR) rank_bases(a, start, rbase);
+  else segment_starts(a, start);
+  finalize_body(a, start, rbase, a.hist_e, a.hist_r, pre);
 }
 
 // Small problems (at most kDirectPer entries per thread of one 1024-thread

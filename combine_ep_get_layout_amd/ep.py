@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libep.so")
 
-MODE_NORMAL, MODE_LOW_LATENCY, MODE_MESSAGES = 0, 1, 2
+MODE_NORMAL, MODE_LOW_LATENCY, MODE_MESSAGES, MODE_RANK_MAJOR = 0, 1, 2, 3
 QUANT_NONE, QUANT_FP8_F32, QUANT_FP8_UE8M0 = 0, 1, 2
 DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY, DEVERR_MESSAGE = 1, 2, 4, 8
 
@@ -53,7 +53,8 @@ class CLayout(ctypes.Structure):
 
 
 class CRecv(ctypes.Structure):
-    _fields_ = [("x", _vp), ("scales", _vp), ("capacity", ctypes.c_int64)]
+    _fields_ = [("x", _vp), ("scales", _vp), ("capacity", ctypes.c_int64),
+                ("topk_idx", _vp), ("topk_weights", _vp)]
 
 
 class CMessages(ctypes.Structure):
@@ -219,9 +220,10 @@ def get_layout(p: Problem, topk_idx: torch.Tensor, layout: Layout, ws: torch.Ten
 
 
 class Recv:
-    """Receive buffers of normal / low-latency dispatch."""
+    """Receive buffers of normal / low-latency / rank-major dispatch.  In
+    rank-major mode `meta` also allocates the per-row top-k ids and weights."""
 
-    def __init__(self, p: Problem, capacity: int, device="cuda"):
+    def __init__(self, p: Problem, capacity: int, device="cuda", meta: bool = True):
         self.capacity = int(capacity)
         if p.quant == QUANT_NONE:
             self.x = torch.empty((self.capacity, p.H), dtype=torch.bfloat16, device=device)
@@ -231,9 +233,16 @@ class Recv:
             n = p.G * (p.E * p.R * p.T if p.mode == MODE_LOW_LATENCY else self.capacity)
             dt = torch.float32 if p.quant == QUANT_FP8_F32 else torch.uint8
             self.scales = torch.empty(max(n, 1), dtype=dt, device=device)
+        self.topk_idx = self.topk_weights = None
+        if p.mode == MODE_RANK_MAJOR and meta:
+            self.topk_idx = torch.empty((max(self.capacity, 1), p.K), dtype=torch.int32,
+                                        device=device)
+            self.topk_weights = torch.empty((max(self.capacity, 1), p.K), dtype=torch.float32,
+                                            device=device)
 
     def c(self) -> CRecv:
-        return CRecv(_ptr(self.x), _ptr(self.scales), self.capacity)
+        return CRecv(_ptr(self.x), _ptr(self.scales), self.capacity, _ptr(self.topk_idx),
+                     _ptr(self.topk_weights))
 
 
 class Messages:
@@ -265,6 +274,14 @@ def dispatch(p: Problem, layout: Layout, x: torch.Tensor, *, recv: Recv | None =
     _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
     if p.mode != MODE_MESSAGES:
         _need(recv is not None and layout.send_pos is not None, "recv buffers and send_pos")
+        if p.mode == MODE_RANK_MAJOR and (recv.topk_idx is not None or recv.topk_weights is not None):
+            _need(topk_idx is not None and topk_idx.dtype == torch.int32
+                  and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32 (row metadata)")
+            _need(recv.topk_weights is None or (topk_weights is not None
+                  and topk_weights.dtype == torch.float32 and topk_weights.numel() == R * T * K),
+                  "topk_weights [R][T][K] fp32 (row metadata)")
+            for t_ in (recv.topk_idx, recv.topk_weights):
+                _need(t_ is None or t_.numel() >= recv.capacity * K, "row metadata [capacity][K]")
         _need(recv.x.shape[0] >= recv.capacity and recv.x.shape[1] == H, "recv x [capacity][H]")
         if p.quant != QUANT_NONE:
             n = p.G * (E * R * T if p.mode == MODE_LOW_LATENCY else recv.capacity)
@@ -295,8 +312,9 @@ def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Ten
             out: torch.Tensor, stream=None) -> None:
     R, T, H, K = p.R, p.T, p.H, p.K
     _need(y.dtype == torch.bfloat16 and y.dim() == 2 and y.shape[1] == H, "y [rows][H] bf16")
-    _need(topk_weights.dtype == torch.float32 and topk_weights.numel() == R * T * K,
-          "topk_weights [R][T][K] fp32")
+    if p.mode != MODE_RANK_MAJOR or topk_weights is not None:
+        _need(topk_weights.dtype == torch.float32 and topk_weights.numel() == R * T * K,
+              "topk_weights [R][T][K] fp32")
     _need(out.dtype == torch.bfloat16 and out.numel() == R * T * H, "out [R][T][H] bf16")
     _need(layout.send_pos is not None and layout.send_pos.numel() == R * T * K, "send_pos")
     cl = layout.c()

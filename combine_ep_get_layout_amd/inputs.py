@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-MODE_NORMAL, MODE_LL, MODE_MSG = 0, 1, 2
+MODE_NORMAL, MODE_LL, MODE_MSG, MODE_RANK = 0, 1, 2, 3
 Q_NONE, Q_FP8_F32, Q_FP8_UE8M0 = 0, 1, 2
 
 
@@ -84,8 +84,11 @@ WORKLOADS = {
                           outlier_scale=50.0, seed=SEED_BASE + 4),
     "messages": Workload("messages", R=64, T=256, H=7168, E=256, K=8, mode=MODE_MSG,
                          quant=Q_FP8_F32, seed=SEED_BASE + 5),
+    # the prefill routing in the rank-major (V1) receive layout
+    "rank_prefill": Workload("rank_prefill", R=8, T=4096, H=7168, E=256, K=8, mode=MODE_RANK,
+                             quant=Q_NONE, routing="zipf", alpha=1.2, seed=SEED_BASE + 3),
 }
-ORDER = ["tiny", "ll_decode", "normal_prefill", "fp8_train", "messages"]
+ORDER = ["tiny", "ll_decode", "normal_prefill", "fp8_train", "messages", "rank_prefill"]
 
 
 def _streams(seed: int):

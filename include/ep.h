@@ -65,6 +65,8 @@ extern "C" {
 #define EP_MODE_NORMAL 0      /* contiguous, expert-major per destination rank */
 #define EP_MODE_LOW_LATENCY 1 /* packed masked: E blocks of R*T rows           */
 #define EP_MODE_MESSAGES 2    /* one packed message per (source, destination)  */
+#define EP_MODE_RANK_MAJOR 3  /* one row per (token, destination rank), in (source, token)
+                                 order per destination: the V1 receive buffer       */
 
 /* payload formats */
 #define EP_QUANT_NONE 0      /* bf16 rows                                      */
@@ -133,6 +135,10 @@ typedef struct ep_recv {
                        low-latency [E][G][R*T].  fp32 (FP8_F32) or uint8 exponents
                        (FP8_UE8M0: scale = 2^(byte - 127)); 4-byte aligned               */
   int64_t capacity; /* rows of x; low-latency needs >= E*R*T                              */
+  int32_t* topk_idx;    /* rank-major only, may be NULL: [capacity][K], the row's token's
+                           experts on this rank as local ids (e - d*L), else -1          */
+  float* topk_weights;  /* rank-major only, may be NULL: [capacity][K], their weights,
+                           else 0                                                       */
 } ep_recv;
 
 /* Send side of message mode. */
@@ -155,7 +161,8 @@ typedef struct ep_messages {
 size_t ep_workspace_bytes(const ep_problem* p);
 
 /* Worst-case receive rows for normal mode (every entry valid, every
- * expert padded by expert_alignment - 1), E*R*T for low-latency. */
+ * expert padded by expert_alignment - 1), E*R*T for low-latency,
+ * R*T*min(K, R) for rank-major (every token on K distinct ranks). */
 int64_t ep_max_recv_rows(const ep_problem* p);
 
 /* Routing layout ("DeepEP" sec. 2.1, 2.3, 3.2, 4.3): histograms per rank
@@ -164,6 +171,13 @@ int64_t ep_max_recv_rows(const ep_problem* p);
  * (send_pos) and of every sent token within its destination stream
  * (send_head).  topk_idx: [R][T][K] int32, -1 = no expert.  Slot order is
  * deterministic: within an expert's segment by (source rank, token, k).
+ * Rank-major mode ("DeepEP" sec. 2.3, the V1 receive buffer and its
+ * address book): partition d holds one row per token with an expert on d,
+ * source s's tokens from row row_base[d] + rank_prefix_matrix[s][d] -
+ * num_tokens_per_rank[s][d] on, in (s, d) stream order (send_head);
+ * send_pos[s][t][k] is the token's row on the rank of expert k;
+ * rows_per_rank / row_base count these rows; expert_start[e] is the first
+ * row of e's rank; recv_src_idx has one entry per row.
  * Resets *err to 0, then may set EP_DEVERR_TOPK_RANGE, _LL_OVERFLOW,
  * _CAPACITY (recv_src_idx too small). */
 int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout* out,
@@ -184,8 +198,13 @@ int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout*
  *   64-byte write descriptors of the payload, header and flag puts, cut at
  *   every region_bytes boundary of either arena.  Uses layout->send_head,
  *   num_tokens_per_rank; `recv` may be NULL.
+ * rank-major: each token is written once per destination rank, to row
+ *   send_pos[s][t][k] (the first k on that rank); when recv->topk_idx /
+ *   topk_weights are given, the row's top-k as that rank sees it (local
+ *   expert ids or -1, weights or 0); FP8 scales column-major [G][capacity].
  * x: [R][T][H] bf16.  topk_idx / topk_weights ([R][T][K]) are read in
- * messages mode only (may be NULL otherwise). */
+ * messages mode, and in rank-major mode for the row metadata (may be NULL
+ * otherwise). */
 int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
                 const int32_t* topk_idx, const float* topk_weights, const ep_recv* recv,
                 const ep_messages* msgs, void* workspace, size_t workspace_bytes,
@@ -195,7 +214,10 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
  * bf16( sum_k topk_weights[s][t][k] * y[send_pos[s][t][k]] ), accumulated in
  * fp32 in k order, rounded to nearest-even; tokens with no routed entry
  * get 0.  y: expert outputs, bf16, in the receive layout ([y_rows][H]).
- * Normal / low-latency modes. */
+ * Normal / low-latency modes.  Rank-major mode: out[s][t] = bf16( sum of
+ * y over the token's distinct rows (one per destination rank), in order of
+ * first k ), unweighted -- the expert stage on each rank has applied the
+ * weights of its experts; topk_weights may be NULL. */
 int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y,
                int64_t y_rows, const float* topk_weights, uint16_t* out, void* stream);
 

@@ -38,6 +38,10 @@ def test_workspace_and_rows_for_workloads():
             assert ep.max_recv_rows(p) == w.E * w.R * w.T
         elif w.mode == ep.MODE_NORMAL:
             assert ep.max_recv_rows(p) == w.R * w.T * w.K
+    pr = ep.Problem(8, 16, 128, 64, 6, mode=ep.MODE_RANK_MAJOR)
+    assert ep.max_recv_rows(pr) == 8 * 16 * 6  # every token on min(K, R) ranks
+    pr = ep.Problem(4, 16, 128, 64, 6, mode=ep.MODE_RANK_MAJOR)
+    assert ep.max_recv_rows(pr) == 4 * 16 * 4
 
 
 @pytest.mark.parametrize("kw,ok", [
@@ -49,7 +53,8 @@ def test_workspace_and_rows_for_workloads():
     (dict(R=4, T=16, H=128, E=16, K=65), False),
     (dict(R=4, T=16, H=128, E=4096, K=2), False),
     (dict(R=4, T=0, H=128, E=16, K=2), True),             # empty input is valid
-    (dict(R=4, T=16, H=128, E=16, K=2, mode=3), False),
+    (dict(R=4, T=16, H=128, E=16, K=2, mode=3), True),     # rank-major
+    (dict(R=4, T=16, H=128, E=16, K=2, mode=4), False),
     (dict(R=4, T=16, H=128, E=16, K=2, quant=7), False),
     (dict(R=4, T=16, H=128, E=16, K=2, align=0), False),
     (dict(R=4, T=16, H=128, E=16, K=2, mode=2, region_bytes=8), False),

@@ -1,0 +1,157 @@
+"""GPU parity of rank-major mode (one receive row per (token, destination
+rank), in (source, token) order per destination) through the C ABI, against
+the oracle: every layout output, every dispatched row, scale and row
+metadata byte for byte, and the combine (an unweighted sum of a token's
+distinct rows) to the fp32-accumulation tolerance.  Small fixed cases, a
+seeded random sweep, and the prefill shape (R8 T4096 H7168 E256 top-8,
+Zipf 1.2) with sampled rows and tokens."""
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_layout_amd import ep, inputs
+from oracle import oracle as orc
+from gpu_util import DEV, LAYOUT_FIELDS, bf16_to_f32, combine_close, h, say
+
+pytestmark = pytest.mark.gpu
+
+RM = ep.MODE_RANK_MAJOR
+FIXED = [
+    # name, R, T, H, E, K, quant, masked, duplicates
+    ("r1", 1, 7, 128, 4, 2, ep.QUANT_NONE, 0.0, 0.0),
+    ("r2_fp8", 2, 19, 256, 8, 3, ep.QUANT_FP8_F32, 0.1, 0.0),
+    ("r4_ue8m0_dups", 4, 33, 256, 16, 8, ep.QUANT_FP8_UE8M0, 0.1, 0.3),
+    ("r8_chunks", 8, 700, 128, 64, 6, ep.QUANT_NONE, 0.05, 0.1),
+    ("r5_odd", 5, 130, 384, 10, 5, ep.QUANT_FP8_F32, 0.2, 0.0),
+    ("r16_wide", 16, 64, 1024, 256, 8, ep.QUANT_NONE, 0.0, 0.0),
+    ("r3_empty", 3, 0, 128, 6, 2, ep.QUANT_NONE, 0.0, 0.0),
+]
+
+
+def draw(i):
+    g = np.random.default_rng(7100 + i)
+    R = int(g.choice([1, 2, 3, 4, 7, 8, 16]))
+    E = R * int(g.integers(1, 9))
+    K = int(g.integers(1, min(E, 10) + 1))
+    T = int(g.choice([1, 5, 64, 257, 1100]))
+    quant = int(g.choice([0, 1, 2]))
+    H = int(8 * g.integers(1, 100)) if quant == 0 else int(128 * g.integers(1, 5))
+    return (f"fuzz{i}", R, T, H, E, K, quant, float(g.choice([0.0, 0.2])),
+            float(g.choice([0.0, 0.3])) if K > 1 else 0.0)
+
+
+CASES = FIXED + [draw(i) for i in range(16)]
+
+
+def run_case(c):
+    name, R, T, H, E, K, quant, mfrac, dfrac = c
+    w = inputs.small(f"rm_{name}", R=R, T=T, H=H, E=E, K=K, mode=RM, quant=quant, seed=83)
+    if T > 0:
+        topk = inputs.gen_topk(w)
+        if mfrac or dfrac:
+            topk = inputs.masked_topk(w, topk, mfrac, dfrac, seed=5)
+        x, wt = inputs.gen_x(w), inputs.gen_weights(w)
+    else:
+        topk = np.zeros((R, 0, K), np.int32)
+        x = np.zeros((R, 0, H), np.uint16)
+        wt = np.zeros((R, 0, K), np.float32)
+    p = ep.Problem(R, T, H, E, K, mode=RM, quant=quant)
+    po = orc.Problem(R, T, H, E, K, mode=RM, quant=quant)
+    return w, p, po, topk, x, wt
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+def test_rank_major_layout_dispatch_combine(c):
+    say("rank-major", c)
+    w, p, po, topk, x, wt = run_case(c)
+    R, T, H, E, K = w.R, w.T, w.H, w.E, w.K
+    ol = orc.layout(po, topk)
+    total = ol.total_rows
+    lay = ep.Layout(p)
+    ws = ep.workspace(p)
+    tk = torch.from_numpy(topk).to(DEV)
+    ep.get_layout(p, tk, lay, ws)
+    torch.cuda.synchronize()
+    for f in LAYOUT_FIELDS:
+        assert np.array_equal(h(getattr(lay, f)), getattr(ol, f)), f
+    assert np.array_equal(h(lay.recv_src_idx)[:total], ol.recv_src_idx[:total])
+    assert int(h(lay.err)[0]) == ol.err == 0
+    # dispatch: rows, scales, per-row top-k ids and weights
+    recv = ep.Recv(p, total)
+    wtg = torch.from_numpy(wt).to(DEV)
+    ep.dispatch(p, lay, torch.from_numpy(x).view(torch.bfloat16).to(DEV), recv=recv,
+                topk_idx=tk, topk_weights=wtg, ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    _, orecv, osc = orc.dispatch(po, x, topk, ol.send_pos, total)
+    g = h(recv.x.view(torch.uint16) if w.quant == ep.QUANT_NONE else recv.x)[:total]
+    assert np.array_equal(g, orecv[:total])
+    if w.quant != ep.QUANT_NONE:
+        assert np.array_equal(h(recv.scales)[: w.G * total], osc[: w.G * total])
+    _, oidx, owts = orc.rank_topk(po, topk, wt, ol.send_pos, total)
+    assert np.array_equal(h(recv.topk_idx)[:total], oidx)
+    assert np.array_equal(h(recv.topk_weights)[:total], owts)
+    # combine: the unweighted sum of each token's rows on its ranks
+    y = inputs.gen_y(w, max(total, 1))
+    out = torch.empty((R, T, H), dtype=torch.bfloat16, device=DEV)
+    ep.combine(p, lay, torch.from_numpy(y).view(torch.bfloat16).to(DEV), None, out)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    _, oout = orc.combine(po, y, wt, ol.send_pos)
+    if out.numel():
+        yf = np.abs(bf16_to_f32(y).astype(np.float64))
+        sp = ol.send_pos.reshape(R * T, K)
+        absw = np.zeros((R * T, H))
+        for i in range(R * T):
+            rows = sorted({int(r) for r in sp[i] if r >= 0})
+            if rows:
+                absw[i] = yf[rows].sum(axis=0)
+        combine_close(h(out.view(torch.uint16)).reshape(-1, H), oout.reshape(-1, H), absw)
+
+
+def test_rank_major_prefill_shape():
+    """R8 T4096 H7168 E256 top-8, Zipf 1.2: the whole layout against the
+    oracle; sampled rows of the dispatch (each holds its source token) and
+    sampled tokens of the combine against the oracle."""
+    w = inputs.WORKLOADS["normal_prefill"].replace(mode=RM)
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    R, T, H, E, K = w.R, w.T, w.H, w.E, w.K
+    p = ep.Problem(R, T, H, E, K, mode=RM)
+    po = orc.Problem(R, T, H, E, K, mode=RM)
+    ol = orc.layout(po, topk)
+    total = ol.total_rows
+    say("rank-major prefill: rows", total)
+    lay = ep.Layout(p, recv_capacity=total)
+    ws = ep.workspace(p)
+    tk = torch.from_numpy(topk).to(DEV)
+    ep.get_layout(p, tk, lay, ws)
+    torch.cuda.synchronize()
+    for f in LAYOUT_FIELDS:
+        assert np.array_equal(h(getattr(lay, f)), getattr(ol, f)), f
+    assert np.array_equal(h(lay.recv_src_idx)[:total], ol.recv_src_idx)
+    recv = ep.Recv(p, total)
+    xg = torch.from_numpy(x).view(torch.bfloat16).to(DEV)
+    ep.dispatch(p, lay, xg, recv=recv, topk_idx=tk, topk_weights=torch.from_numpy(wt).to(DEV),
+                ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    rng = np.random.default_rng(9)
+    rows = rng.choice(total, 4096, replace=False)
+    src = ol.recv_src_idx[rows]
+    got = h(recv.x[torch.from_numpy(rows).to(DEV)].view(torch.uint16))
+    assert np.array_equal(got, x.reshape(-1, H)[src])
+    _, oidx, owts = orc.rank_topk(po, topk, wt, ol.send_pos, total)
+    assert np.array_equal(h(recv.topk_idx)[:total], oidx)
+    assert np.array_equal(h(recv.topk_weights)[:total], owts)
+    # combine of random per-rank rows, sampled tokens
+    y = inputs.gen_y(w, total)
+    out = torch.empty((R, T, H), dtype=torch.bfloat16, device=DEV)
+    ep.combine(p, lay, torch.from_numpy(y).view(torch.bfloat16).to(DEV), None, out)
+    torch.cuda.synchronize()
+    toks = rng.choice(R * T, 512, replace=False)
+    _, oout = orc.combine(po, y, wt, ol.send_pos, tokens=toks)
+    yf = np.abs(bf16_to_f32(y).astype(np.float64))
+    sp = ol.send_pos.reshape(R * T, K)
+    absw = np.stack([yf[sorted({int(r) for r in sp[i] if r >= 0})].sum(axis=0) for i in toks])
+    g = h(out.view(torch.uint16)).reshape(-1, H)[toks]
+    combine_close(g, oout, absw)
