@@ -74,10 +74,23 @@ def combine_bytes(w, rows=None):
     return 2 * H * M + 2 * H * N + 8 * M
 
 
-def kernel_hash():
+# sources each profiled kernel is built from (its counters go stale when
+# any of them changes)
+KERNEL_SOURCES = {
+    "dispatch_copy": ["dispatch.hip", "ep_device.hpp", "ep_internal.hpp"],
+    "dispatch_fp8": ["dispatch.hip", "quant.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "combine_rows": ["combine.hip", "ep_device.hpp", "ep_internal.hpp"],
+    "msg_pack_fp8": ["messages.hip", "msg_format.hpp", "quant.hpp", "ep_device.hpp",
+                     "ep_internal.hpp"],
+    "msg_pack_bf16": ["messages.hip", "msg_format.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "msg_exec_puts": ["receive.hip", "msg_format.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "msg_unpack": ["receive.hip", "msg_format.hpp", "ep_device.hpp", "ep_internal.hpp"],
+}
+
+
+def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in ["dispatch.hip", "combine.hip", "messages.hip", "receive.hip", "msg_format.hpp",
-              "quant.hpp", "ep_device.hpp"]:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -92,7 +105,7 @@ def traffic_from_profile(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     e = d.get(f"{workload}:{kernel}")
-    if not e or e.get("kernel_hash") != kernel_hash():
+    if not e or e.get("kernel_hash") != kernel_hash(kernel):
         return None
     return e.get("hbm_bytes_per_launch")
 

@@ -106,7 +106,7 @@ def main():
                           "msg_pack_bf16", "msg_exec_puts", "msg_unpack"):
                 if short in k:
                     d[f"{args.workload}:{short}"] = {"hbm_bytes_per_launch": round(v), "kernel": k,
-                                                     "kernel_hash": kernel_hash(),
+                                                     "kernel_hash": kernel_hash(short),
                                                      "title": args.title}
         json.dump(d, open(args.json, "w"), indent=1)
     print("\n".join(lines))
