@@ -113,8 +113,9 @@ def traffic_from_profile(kernel: str, workload: str):
 class Runner:
     """Buffers and launches of one workload; everything resident in HBM."""
 
-    def __init__(self, w, torch, ep, inputs, keep_host=False):
+    def __init__(self, w, torch, ep, inputs, keep_host=False, fused=False):
         self.w, self.torch, self.ep = w, torch, ep
+        self.fused = fused and w.mode in (ep.MODE_NORMAL, ep.MODE_LOW_LATENCY)
         dev = "cuda"
         log(f"[bench] {w.name}: generating inputs")
         topk = inputs.gen_topk(w)
@@ -181,6 +182,11 @@ class Runner:
                       "combine": combine_bytes(w, self.rows)}
         self.kernels = {"dispatch": "dispatch_copy" if w.quant == 0 else "dispatch_fp8",
                         "combine": "combine_rows"}
+        if self.fused:
+            lb = self.bytes.pop("layout")
+            self.bytes = {"layout+dispatch": lb + self.bytes["dispatch"],
+                          "combine": self.bytes["combine"]}
+            self.kernels = {"layout+dispatch": self.kernels["dispatch"], "combine": "combine_rows"}
         self.extra = {}
 
     def phases(self):
@@ -198,6 +204,10 @@ class Runner:
             ph.append(("unpack", lambda: ep.messages_unpack(p, self.msgs, self.recv_arena,
                                                             self.lay.num_tokens_per_expert,
                                                             *self.unp, self.err)))
+        elif self.fused:  # layout and dispatch in one call
+            ph = [("layout+dispatch", lambda: ep.dispatch_fused(p, self.topk, self.lay, self.x,
+                                                                self.recv, self.ws)),
+                  ("combine", lambda: ep.combine(p, self.lay, self.y, self.wt, self.out))]
         else:
             if self.w.mode == ep.MODE_RANK_MAJOR:  # rows plus their top-k metadata
                 ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
@@ -340,6 +350,8 @@ def main():
                     help="comma-separated; the first is the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch in one call (ep_dispatch_fused)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain copy of 2^30 bytes (counter calibration)")
     args = ap.parse_args()
@@ -359,7 +371,7 @@ def main():
     cpu = None
     for i, name in enumerate(names):
         w = inputs.WORKLOADS[name]
-        r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu))
+        r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu), fused=args.fused)
         steps = args.steps if i == 0 else max(5, min(args.steps, 20))
         ms, res = r.report(steps, args.warmup)
         if i == 0:

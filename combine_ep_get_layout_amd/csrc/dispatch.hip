@@ -16,6 +16,7 @@
 // sits at the chip's write-dominated bandwidth.)
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "layout_rows.hpp"
 #include "quant.hpp"
 
 namespace ep {
@@ -74,19 +75,84 @@ __device__ __forceinline__ void write_row_meta(const RowMeta& m, int K, int64_t 
   if (m.wts) m.wts[row * K + lane] = on ? myw : 0.0f;
 }
 
-template <int NV, bool RM>
+// Layout fused into dispatch ("DeepEP" deep dive, sec. 4.6: V2 moves the
+// layout's last step into the dispatch kernel).  The block of token `tok`
+// derives the token's K rows from the scanned chunk histograms (lanes
+// k < K hold row k); the writer wave also stores the layout's per-token
+// outputs (send_pos, recv_src_idx, send_head).  `start` = segment starts
+// (LDS) in normal mode; low-latency blocks are fixed at e * R*T.
+__device__ __forceinline__ int fused_token_rows(const LayoutArgs& a, int64_t tok, bool writer,
+                                                const int* start) {
+  const Geometry& g = a.g;
+  const int lane = lane_id();
+  int row = -1;
+  if (lane < g.K) {
+    const int64_t i = tok * g.K + lane;
+    const int e = a.topk[i];
+    const int local = a.local_e[i];
+    if (writer && (e < -1 || e >= g.E)) set_err(a.err, EP_DEVERR_TOPK_RANGE);
+    if (local >= 0) {
+      const int start_e = a.mode == EP_MODE_LOW_LATENCY ? e * g.R * g.T : start[e];
+      row = entry_row(a, start_e, a.hist_e, tok, e, local);
+    }
+    if (writer) {
+      if (a.send_pos) a.send_pos[i] = row;
+      if (row >= 0 && a.recv_src_idx) {
+        if (row < a.recv_cap) a.recv_src_idx[row] = (int)tok;
+        else set_err(a.err, EP_DEVERR_CAPACITY);
+      }
+    }
+  }
+  if (writer && a.send_head)
+    for (int d = lane; d < g.R; d += kWave) {
+      const int64_t hi = tok * g.R + d;
+      a.send_head[hi] = stream_index(a, a.hist_r, tok, d, a.local_r[hi]);
+    }
+  return row;
+}
+
+// The layout's per-expert and per-rank outputs, written by block b for
+// expert b (and rank b), plus the alignment padding rows of expert b's
+// segment.  Every block of a fused dispatch calls this first.
+__device__ __forceinline__ void fused_publish(const LayoutArgs& a, const int* start) {
+  const Geometry& g = a.g;
+  const int b = blockIdx.x;
+  const bool ll = a.mode == EP_MODE_LOW_LATENCY;
+  const int rt = g.R * g.T;
+  if (b < g.E && threadIdx.x == 0) a.expert_start[b] = ll ? b * rt : start[b];
+  if (b <= g.R && threadIdx.x == 0) {
+    const int base = ll ? b * g.L * rt : start[b * g.L];
+    a.row_base[b] = base;
+    if (b < g.R) a.rows[b] = ll ? g.L * rt : start[(b + 1) * g.L] - base;
+  }
+  if (!ll && b < g.E && a.recv_src_idx && a.align > 1) {
+    const int first = start[b] + a.recv_per_expert[b];
+    for (int r = first + (int)threadIdx.x; r < start[b + 1]; r += blockDim.x)
+      if (r < a.recv_cap) a.recv_src_idx[r] = -1;
+  }
+}
+
+template <int NV, bool RM, bool FU>
 __global__ __launch_bounds__(1024) void dispatch_copy(const u32x4* __restrict__ x,
                                                       const int32_t* __restrict__ send_pos,
                                                       u32x4* __restrict__ recv, int V, int K,
-                                                      int64_t cap, int32_t* err, RowMeta meta) {
+                                                      int64_t cap, int32_t* err, RowMeta meta,
+                                                      LayoutArgs la) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x;
   const int base = uniform(threadIdx.x >> 6) * kWave * NV;
+  __shared__ int start[FU ? 2049 : 1];
+  if (FU) {
+    if (la.mode != EP_MODE_LOW_LATENCY) segment_starts(la, start);
+    fused_publish(la, start);
+    if (tok >= la.g.R * la.g.T) return;  // publishing-only block
+  }
   const u32x4* src = x + (int64_t)tok * V;
   u32x4 v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = src[min(base + lane + kWave * i, V - 1)];  // in bounds
-  const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
+  const int myrow = FU ? fused_token_rows(la, tok, base == 0, start)
+                       : (lane < K ? send_pos[(int64_t)tok * K + lane] : -1);
   // rank-major: each destination row once; the first wave writes its metadata
   const uint64_t keep = RM ? first_of_rows(myrow, K) : ~0ull;
   const bool meta_wave = RM && base == 0 && (meta.idx || meta.wts);
@@ -124,14 +190,21 @@ __device__ __forceinline__ int xcd_run(int b, int n) {
   return (b % kXcds) * per + b / kXcds;
 }
 
-template <int NP, int Q, bool LL, bool RM>
+template <int NP, int Q, bool LL, bool RM, bool FU>
 __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ send_pos,
                                                      u32x4* __restrict__ codes,
                                                      void* __restrict__ scales, int P, int K,
                                                      int64_t cap, int G, int RT, int n_tok,
-                                                     int32_t* err, RowMeta meta) {
+                                                     int32_t* err, RowMeta meta, LayoutArgs la) {
   const int lane = threadIdx.x & 63;
+  __shared__ int start[FU && !LL ? 2049 : 1];
+  if (FU) {
+    if (!LL) segment_starts(la, start);
+    fused_publish(la, start);
+  }
+  // blocks past the token grid only publish (fused), never alias a token
+  if ((int)blockIdx.x >= (LL ? kXcds * ((n_tok + kXcds - 1) / kXcds) : n_tok)) return;
   // low-latency: die blockIdx.x % kXcds takes a contiguous run of tokens, so
   // consecutive slots of an expert (consecutive tokens) are stored from one
   // L2 and their 4-byte column-major scales merge into whole lines there
@@ -146,7 +219,8 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
   uint32_t sce[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) quantise_pair<Q>(lo[i], hi[i], cv[i], scf[i], sce[i]);
-  const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
+  const int myrow = FU ? fused_token_rows(la, tok, base == 0, start)
+                       : (lane < K ? send_pos[(int64_t)tok * K + lane] : -1);
   // rank-major: each destination row once; the first wave writes its metadata
   const uint64_t keep = RM ? first_of_rows(myrow, K) : ~0ull;
   const bool meta_wave = RM && base == 0 && (meta.idx || meta.wts);
@@ -261,12 +335,27 @@ inline RowMeta row_meta(const DispatchArgs& a) {
   return m;
 }
 
+// A fused dispatch also needs one block per expert and per rank boundary
+// to publish the layout's per-expert outputs.
+inline int fused_blocks(const DispatchArgs& a, int blocks) {
+  if (!a.fused) return blocks;
+  int b = blocks;
+  if (b < a.g.E) b = a.g.E;
+  if (b < a.g.R + 1) b = a.g.R + 1;
+  return b;
+}
+
 template <int NV, bool RM>
 static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
-  hipLaunchKernelGGL((dispatch_copy<NV, RM>), dim3(N), dim3(kWave * waves), 0, st,
-                     (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
-                     row_meta(a));
+  if (a.fused)
+    hipLaunchKernelGGL((dispatch_copy<NV, false, true>), dim3(fused_blocks(a, N)),
+                       dim3(kWave * waves), 0, st, (const u32x4*)a.x, a.send_pos,
+                       (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err, row_meta(a), a.la);
+  else
+    hipLaunchKernelGGL((dispatch_copy<NV, RM, false>), dim3(N), dim3(kWave * waves), 0, st,
+                       (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
+                       row_meta(a), a.la);
 }
 
 template <int NP, int Q, bool LL, bool RM>
@@ -276,10 +365,16 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
   // stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
   const int blocks = LL ? kXcds * ((N + kXcds - 1) / kXcds) : N;
-  hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, RM>), dim3(blocks), dim3(kWave * waves), 0, st,
-                     (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
-                     LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
-                     a.err, row_meta(a));
+  if (a.fused && !RM)
+    hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, false, true>), dim3(fused_blocks(a, blocks)),
+                       dim3(kWave * waves), 0, st, (const u32x4*)a.x, a.send_pos,
+                       (u32x4*)a.recv_x, LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G,
+                       a.g.R * a.g.T, N, a.err, row_meta(a), a.la);
+  else
+    hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, RM, false>), dim3(blocks), dim3(kWave * waves),
+                       0, st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
+                       LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
+                       a.err, row_meta(a), a.la);
   if (!LL) {
     // 64 rows per tile, fewer for wide rows (the tile lives in LDS)
     const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;

@@ -139,11 +139,14 @@ const char* ep_status_string(int s) {
   }
 }
 
-int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout* out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  Geometry g;
-  int st = ep::make_geometry(p, &g);
-  if (st != EP_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks ep_get_layout's arguments and fills the kernel arguments.
+int layout_args(const ep_problem* p, const Geometry& g, const int32_t* topk_idx,
+                const ep_layout* out, void* workspace, size_t workspace_bytes,
+                ep::LayoutArgs* a) {
   // arrays with one entry per token may be NULL when there are no tokens
   const bool toks = (int64_t)g.R * g.T > 0;
   if (!out || !out->num_tokens_per_rank || !out->num_tokens_per_expert ||
@@ -163,30 +166,107 @@ int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout*
   if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
   if (out->recv_src_idx && out->recv_capacity < 0) return EP_ERR_CAPACITY;
 
-  ep::LayoutArgs a;
-  memset(&a, 0, sizeof(a));
-  a.g = g;
-  a.mode = p->mode;
-  a.align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;
-  a.topk = topk_idx;
-  a.cnt_rank = out->num_tokens_per_rank;
-  a.cnt_expert = out->num_tokens_per_expert;
-  a.in_rank = out->is_token_in_rank;
-  a.rpm = out->rank_prefix_matrix;
-  a.recv_per_expert = out->recv_tokens_per_expert;
-  a.expert_start = out->expert_start;
-  a.rows = out->rows_per_rank;
-  a.row_base = out->row_base;
-  a.send_pos = out->send_pos;
-  a.send_head = out->send_head;
-  a.recv_src_idx = out->recv_src_idx;
-  a.recv_cap = out->recv_capacity;
-  a.err = out->err;
+  memset(a, 0, sizeof(*a));
+  a->g = g;
+  a->mode = p->mode;
+  a->align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;
+  a->topk = topk_idx;
+  a->cnt_rank = out->num_tokens_per_rank;
+  a->cnt_expert = out->num_tokens_per_expert;
+  a->in_rank = out->is_token_in_rank;
+  a->rpm = out->rank_prefix_matrix;
+  a->recv_per_expert = out->recv_tokens_per_expert;
+  a->expert_start = out->expert_start;
+  a->rows = out->rows_per_rank;
+  a->row_base = out->row_base;
+  a->send_pos = out->send_pos;
+  a->send_head = out->send_head;
+  a->recv_src_idx = out->recv_src_idx;
+  a->recv_cap = out->recv_capacity;
+  a->err = out->err;
   char* ws = (char*)workspace;
-  a.hist_e = (int32_t*)(ws + g.off_hist_e);
-  a.hist_r = (int32_t*)(ws + g.off_hist_r);
-  a.local_e = (int32_t*)(ws + g.off_local_e);
-  a.local_r = (int32_t*)(ws + g.off_local_r);
+  a->hist_e = (int32_t*)(ws + g.off_hist_e);
+  a->hist_r = (int32_t*)(ws + g.off_hist_r);
+  a->local_e = (int32_t*)(ws + g.off_local_e);
+  a->local_r = (int32_t*)(ws + g.off_local_r);
+  return EP_OK;
+}
+
+// Checks ep_dispatch's arguments for the normal, low-latency and
+// rank-major modes and fills the kernel arguments.
+int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layout,
+                  const uint16_t* x, const int32_t* topk_idx, const float* topk_weights,
+                  const ep_recv* recv, void* workspace, size_t workspace_bytes,
+                  ep::DispatchArgs* a) {
+  const bool toks = (int64_t)g.R * g.T > 0;
+  memset(a, 0, sizeof(*a));
+  if (!recv) return EP_ERR_NULL;
+  // receive buffers may be NULL when they have no rows
+  const bool rows = recv->capacity > 0;
+  if (toks && !layout->send_pos) return EP_ERR_NULL;
+  if (toks && rows && !recv->x) return EP_ERR_NULL;
+  if (toks && rows && p->quant != EP_QUANT_NONE && !recv->scales) return EP_ERR_NULL;
+  if (!aligned(recv->x, 16) || !aligned(layout->send_pos, 4)) return EP_ERR_ALIGN;
+  if (recv->scales && !aligned(recv->scales, 4)) return EP_ERR_ALIGN;
+  if (recv->capacity < 0) return EP_ERR_CAPACITY;
+  if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
+    return EP_ERR_CAPACITY;
+  const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;
+  const bool staged =
+      (p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE;
+  if (rank_major && toks) {
+    // per-row metadata needs the routing (ids) and, for weights, the weights
+    if ((recv->topk_idx || recv->topk_weights) && !topk_idx) return EP_ERR_NULL;
+    if (recv->topk_weights && !topk_weights) return EP_ERR_NULL;
+    if (!aligned(recv->topk_idx, 4) || !aligned(recv->topk_weights, 4) ||
+        !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
+      return EP_ERR_ALIGN;
+  }
+  if (staged && toks) {
+    if (!workspace || !layout->expert_start || !layout->recv_tokens_per_expert ||
+        !layout->row_base)
+      return EP_ERR_NULL;
+    if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
+    if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
+  }
+  
+  a->g = g;
+  a->mode = p->mode;
+  a->quant = p->quant;
+  a->stage = staged ? (char*)workspace + g.off_stage : nullptr;
+  a->stage_rows = rank_major ? (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R)
+                            : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+  a->rank_major = rank_major;
+  a->topk = rank_major ? topk_idx : nullptr;
+  a->w = rank_major ? topk_weights : nullptr;
+  a->recv_topk_idx = rank_major ? recv->topk_idx : nullptr;
+  a->recv_topk_weights = rank_major ? recv->topk_weights : nullptr;
+  a->expert_start = layout->expert_start;
+  a->recv_per_expert = layout->recv_tokens_per_expert;
+  a->row_base = layout->row_base;
+  a->x = x;
+  a->send_pos = layout->send_pos;
+  a->recv_x = recv->x;
+  a->recv_scales = recv->scales;
+  a->cap = recv->capacity;
+  // low-latency rows never leave the E blocks of R*T rows the scales cover
+  if (p->mode == EP_MODE_LOW_LATENCY) a->cap = (int64_t)g.E * g.R * g.T;
+  a->err = layout->err;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_get_layout(const ep_problem* p, const int32_t* topk_idx, const ep_layout* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  ep::LayoutArgs a;
+  st = layout_args(p, g, topk_idx, out, workspace, workspace_bytes, &a);
+  if (st != EP_OK) return st;
   if (ep::launch_layout(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
   return EP_OK;
 }
@@ -201,58 +281,10 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
   if (!layout || !layout->err || (toks && !x)) return EP_ERR_NULL;
   if (!aligned(x, 16) || !aligned(layout->err, 4)) return EP_ERR_ALIGN;
   if (p->mode != EP_MODE_MESSAGES) {
-    if (!recv) return EP_ERR_NULL;
-    // receive buffers may be NULL when they have no rows
-    const bool rows = recv->capacity > 0;
-    if (toks && !layout->send_pos) return EP_ERR_NULL;
-    if (toks && rows && !recv->x) return EP_ERR_NULL;
-    if (toks && rows && p->quant != EP_QUANT_NONE && !recv->scales) return EP_ERR_NULL;
-    if (!aligned(recv->x, 16) || !aligned(layout->send_pos, 4)) return EP_ERR_ALIGN;
-    if (recv->scales && !aligned(recv->scales, 4)) return EP_ERR_ALIGN;
-    if (recv->capacity < 0) return EP_ERR_CAPACITY;
-    if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
-      return EP_ERR_CAPACITY;
-    const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;
-    const bool staged =
-        (p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE;
-    if (rank_major && toks) {
-      // per-row metadata needs the routing (ids) and, for weights, the weights
-      if ((recv->topk_idx || recv->topk_weights) && !topk_idx) return EP_ERR_NULL;
-      if (recv->topk_weights && !topk_weights) return EP_ERR_NULL;
-      if (!aligned(recv->topk_idx, 4) || !aligned(recv->topk_weights, 4) ||
-          !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
-        return EP_ERR_ALIGN;
-    }
-    if (staged && toks) {
-      if (!workspace || !layout->expert_start || !layout->recv_tokens_per_expert ||
-          !layout->row_base)
-        return EP_ERR_NULL;
-      if (!aligned(workspace, 16)) return EP_ERR_ALIGN;
-      if (workspace_bytes < g.ws_bytes) return EP_ERR_WORKSPACE;
-    }
     ep::DispatchArgs a;
-    a.g = g;
-    a.mode = p->mode;
-    a.quant = p->quant;
-    a.stage = staged ? (char*)workspace + g.off_stage : nullptr;
-    a.stage_rows = rank_major ? (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R)
-                              : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
-    a.rank_major = rank_major;
-    a.topk = rank_major ? topk_idx : nullptr;
-    a.w = rank_major ? topk_weights : nullptr;
-    a.recv_topk_idx = rank_major ? recv->topk_idx : nullptr;
-    a.recv_topk_weights = rank_major ? recv->topk_weights : nullptr;
-    a.expert_start = layout->expert_start;
-    a.recv_per_expert = layout->recv_tokens_per_expert;
-    a.row_base = layout->row_base;
-    a.x = x;
-    a.send_pos = layout->send_pos;
-    a.recv_x = recv->x;
-    a.recv_scales = recv->scales;
-    a.cap = recv->capacity;
-    // low-latency rows never leave the E blocks of R*T rows the scales cover
-    if (p->mode == EP_MODE_LOW_LATENCY) a.cap = (int64_t)g.E * g.R * g.T;
-    a.err = layout->err;
+    st = dispatch_args(p, g, layout, x, topk_idx, topk_weights, recv, workspace,
+                       workspace_bytes, &a);
+    if (st != EP_OK) return st;
     if (ep::launch_dispatch(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
     return EP_OK;
   }
@@ -289,6 +321,34 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
   a.err = layout->err;
   a.ws = (char*)workspace + g.off_msg;
   if (ep::launch_messages(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}
+
+int ep_dispatch_fused(const ep_problem* p, const int32_t* topk_idx, const ep_layout* layout,
+                      const uint16_t* x, const ep_recv* recv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  Geometry g;
+  int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (p->mode != EP_MODE_NORMAL && p->mode != EP_MODE_LOW_LATENCY) return EP_ERR_MODE;
+  const bool toks = (int64_t)g.R * g.T > 0;
+  if (!layout || !layout->err || (toks && !x)) return EP_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(layout->err, 4)) return EP_ERR_ALIGN;
+  ep::LayoutArgs la;
+  st = layout_args(p, g, topk_idx, layout, workspace, workspace_bytes, &la);
+  if (st != EP_OK) return st;
+  ep::DispatchArgs a;
+  st = dispatch_args(p, g, layout, x, topk_idx, nullptr, recv, workspace, workspace_bytes, &a);
+  if (st != EP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (g.direct || !toks) {  // small problems: the one-launch layout, then dispatch
+    if (ep::launch_layout(la, s) != hipSuccess) return EP_ERR_HIP;
+  } else {
+    if (ep::launch_layout_counts(la, s) != hipSuccess) return EP_ERR_HIP;
+    a.fused = true;
+    a.la = la;
+  }
+  if (ep::launch_dispatch(a, s) != hipSuccess) return EP_ERR_HIP;
   return EP_OK;
 }
 

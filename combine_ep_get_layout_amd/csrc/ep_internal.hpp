@@ -54,6 +54,9 @@ struct LayoutArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+// The counting and scanning launches only (chunked path), for dispatch
+// kernels that take the final step themselves.
+hipError_t launch_layout_counts(const LayoutArgs& a, hipStream_t stream);
 
 struct DispatchArgs {
   Geometry g;
@@ -78,6 +81,11 @@ struct DispatchArgs {
   const float* w;
   int32_t* recv_topk_idx;
   float* recv_topk_weights;
+  // layout fused into dispatch: the kernel derives each token's rows from
+  // the scanned chunk histograms (la) instead of reading send_pos, and
+  // writes the layout's remaining outputs itself
+  bool fused;
+  LayoutArgs la;
 };
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);

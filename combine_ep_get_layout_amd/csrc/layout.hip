@@ -25,6 +25,7 @@
 //                starts, rows per rank and row bases.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
+#include "layout_rows.hpp"
 
 namespace ep {
 
@@ -120,29 +121,6 @@ __global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
   for (int d = lane; d < g.R; d += kWave) a.hist_r[(int64_t)d * g.NC + chunk] = cnt_r[d];
 }
 
-// Exclusive block scan of one int per thread (up to 1024 threads); returns
-// the exclusive prefix, *total receives the block sum.
-__device__ int block_exclusive_scan(int v, int* total) {
-  __shared__ int wsum[16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(incl, o);
-    if (lane >= o) incl += n;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) before += wsum[w];
-    all += wsum[w];
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 // Exclusive scan, in place, of a row of n = nseg * seg ints; seg_start[j]
 // (LDS) receives the prefix at the start of segment j and seg_start[nseg]
 // the total.  With `relative`, each element is then made relative to its
@@ -197,58 +175,6 @@ __global__ __launch_bounds__(1024) void layout_scan(LayoutArgs a) {
   }
 }
 
-// Segment starts in LDS: start[e] for e in [0, E].  Every block of the
-// finalize launch computes them itself from the per-expert receive counts
-// (an exclusive scan of the counts rounded up to expert_alignment; fixed
-// blocks of R*T rows in low-latency mode).
-// Rank-major mode: partition bases in rbase[0..R] (exclusive scan of the
-// rows each rank receives, the last row of the rank prefix matrix), and
-// start[e] = base of e's rank.
-__device__ void rank_bases(const LayoutArgs& a, int* start, int* rbase) {
-  const Geometry& g = a.g;
-  const int per = (g.R + blockDim.x - 1) / blockDim.x;
-  const int lo = min(g.R, (int)threadIdx.x * per), hi = min(g.R, lo + per);
-  int sum = 0;
-  for (int d = lo; d < hi; ++d) sum += a.rpm[(g.R - 1) * g.R + d];
-  int total;
-  int run = block_exclusive_scan(sum, &total);
-  for (int d = lo; d < hi; ++d) {
-    rbase[d] = run;
-    run += a.rpm[(g.R - 1) * g.R + d];
-  }
-  if (threadIdx.x == 0) rbase[g.R] = total;
-  __syncthreads();
-  for (int e = threadIdx.x; e < g.E; e += blockDim.x) start[e] = rbase[e / g.L];
-  if (threadIdx.x == 0) start[g.E] = total;
-  __syncthreads();
-}
-
-__device__ void segment_starts(const LayoutArgs& a, int* start) {
-  const Geometry& g = a.g;
-  if (a.mode == EP_MODE_LOW_LATENCY) {
-    const int rt = g.R * g.T;
-    for (int e = threadIdx.x; e <= g.E; e += blockDim.x) start[e] = e * rt;
-    __syncthreads();
-    return;
-  }
-  const int per = (g.E + blockDim.x - 1) / blockDim.x;
-  const int lo = min(g.E, (int)threadIdx.x * per), hi = min(g.E, lo + per);
-  int sum = 0;
-  for (int e = lo; e < hi; ++e) {
-    const int n = a.recv_per_expert[e];
-    sum += (n + a.align - 1) / a.align * a.align;
-  }
-  int total;
-  int run = block_exclusive_scan(sum, &total);
-  for (int e = lo; e < hi; ++e) {
-    start[e] = run;
-    const int n = a.recv_per_expert[e];
-    run += (n + a.align - 1) / a.align * a.align;
-  }
-  if (threadIdx.x == 0) start[g.E] = total;
-  __syncthreads();
-}
-
 // Slots: row = segment start + (source, chunk) prefix + rank in chunk, and
 // the token streams' indices.  Block 0 also publishes the segment starts,
 // rows per rank and row bases; padding rows get recv_src_idx = -1.
@@ -282,7 +208,6 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int* 
   // rank-major rows come from the stream indices, needed even without send_head
   const int64_t n_head = (a.send_head || rank_major) ? (int64_t)g.R * g.T * g.R : 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int rt = g.R * g.T;
   // one index walks both the (token, k) entries and the (token, rank) heads,
   // so their chunk-prefix gathers are in flight together
   const int64_t n_all = n_ent > n_head ? n_ent : n_head;
@@ -305,15 +230,10 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int* 
           const int head = a.local_r[hi] + hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
           row = rbase[d] + a.rpm[s * g.R + d] - a.cnt_rank[s * g.R + d] + head;
         } else {
-          const int pos = hist_e[(int64_t)e * g.NC + s * g.C + t / g.ct] + local;
-          if (a.mode == EP_MODE_LOW_LATENCY && pos >= rt) {
-            set_err(a.err, EP_DEVERR_LL_OVERFLOW);
-          } else {
-            row = start[e] + pos;
-            if (a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
-              if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
-              else set_err(a.err, EP_DEVERR_CAPACITY);
-            }
+          row = entry_row(a, start[e], hist_e, st, e, local);
+          if (row >= 0 && a.mode != EP_MODE_MESSAGES && a.recv_src_idx) {
+            if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
+            else set_err(a.err, EP_DEVERR_CAPACITY);
           }
         }
       }
@@ -323,8 +243,8 @@ __device__ void finalize_body(const LayoutArgs& a, const int* start, const int* 
       if (v >= 0) {
         const int64_t st = i / g.R;
         const int d = (int)(i % g.R);
-        const int s = (int)(st / g.T), t = (int)(st % g.T);
-        v += hist_r[(int64_t)d * g.NC + s * g.C + t / g.ct];
+        const int s = (int)(st / g.T);
+        v = stream_index(a, hist_r, st, d, v);
         if (rank_major && a.recv_src_idx) {
           const int row = rbase[d] + a.rpm[s * g.R + d] - a.cnt_rank[s * g.R + d] + v;
           if (row < a.recv_cap) a.recv_src_idx[row] = (int)st;
@@ -607,13 +527,8 @@ __global__ __launch_bounds__(kDirectThreads) void layout_direct(LayoutArgs a) {
     direct_rank_block(a, blockIdx.x - eb, src_prefix[0]);
 }
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+hipError_t launch_layout_counts(const LayoutArgs& a, hipStream_t stream) {
   const Geometry& g = a.g;
-  if (g.direct && (int64_t)g.R * g.T * g.K <= (int64_t)kDirectPer * kDirectThreads) {
-    const int eb = (g.E + kDirectExperts - 1) / kDirectExperts;
-    hipLaunchKernelGGL(layout_direct, dim3(eb + g.R), dim3(kDirectThreads), 0, stream, a);
-    return hipGetLastError();
-  }
   // LDS per wavefront: expert and rank counters plus one batch of rows;
   // at most 64 KiB per block
   const size_t per_wave = sizeof(int32_t) * (size_t)(g.E + g.R + g.tb * g.R);
@@ -628,6 +543,18 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (scan_threads < 256) scan_threads = 256;
   if (scan_threads > 1024) scan_threads = 1024;
   hipLaunchKernelGGL(layout_scan, dim3(g.E + g.R), dim3(scan_threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+  const Geometry& g = a.g;
+  if (g.direct && (int64_t)g.R * g.T * g.K <= (int64_t)kDirectPer * kDirectThreads) {
+    const int eb = (g.E + kDirectExperts - 1) / kDirectExperts;
+    hipLaunchKernelGGL(layout_direct, dim3(eb + g.R), dim3(kDirectThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_layout_counts(a, stream);
+  if (e != hipSuccess) return e;
   const int64_t work = (int64_t)g.R * g.T * (g.K > g.R ? g.K : g.R);
   int64_t fb = (work + 255) / 256;
   if (fb > 4096) fb = 4096;

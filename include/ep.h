@@ -210,6 +210,18 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
                 const ep_messages* msgs, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* Layout and dispatch in one call ("DeepEP" sec. 4.6: V2 folds the
+ * layout's notify step into the dispatch kernel): the outputs of
+ * ep_get_layout and of ep_dispatch, with the last step of the layout (each
+ * entry's row, send_pos, recv_src_idx, send_head, the segment starts) taken
+ * by the dispatch kernel itself, so the call issues three launches instead
+ * of four (two for problems small enough for the one-launch layout).
+ * Arguments as for ep_get_layout and ep_dispatch; normal and low-latency
+ * modes (EP_ERR_MODE otherwise).  The workspace is used by both steps. */
+int ep_dispatch_fused(const ep_problem* p, const int32_t* topk_idx, const ep_layout* layout,
+                      const uint16_t* x, const ep_recv* recv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Combine ("DeepEP" sec. 2.3: the handle walked backwards): out[s][t] =
  * bf16( sum_k topk_weights[s][t][k] * y[send_pos[s][t][k]] ), accumulated in
  * fp32 in k order, rounded to nearest-even; tokens with no routed entry

@@ -1,0 +1,113 @@
+"""GPU parity of ep_dispatch_fused (layout and dispatch in one call, the
+layout's last step taken by the dispatch kernel) through the C ABI: every
+layout output and every dispatched row and scale equal those of separate
+ep_get_layout + ep_dispatch calls bit for bit, and the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_layout_amd import ep, inputs
+from oracle import oracle as orc
+from gpu_util import DEV, LAYOUT_FIELDS, assert_layout_equal, h, say
+
+pytestmark = pytest.mark.gpu
+
+N, L, QF, QU = ep.MODE_NORMAL, ep.MODE_LOW_LATENCY, ep.QUANT_FP8_F32, ep.QUANT_FP8_UE8M0
+CASES = [
+    # name, R, T, H, E, K, mode, quant, align, masked, duplicates
+    ("small_direct", 2, 17, 256, 8, 3, N, 0, 1, 0.1, 0.0),
+    ("normal_bf16", 4, 700, 128, 32, 6, N, 0, 1, 0.0, 0.0),
+    ("normal_align", 4, 500, 256, 16, 4, N, QF, 4, 0.2, 0.0),
+    ("normal_ue8m0", 8, 300, 384, 64, 8, N, QU, 2, 0.05, 0.1),
+    ("ll_fp8", 8, 128, 512, 64, 8, L, QF, 1, 0.0, 0.0),
+    ("ll_bf16_dups", 4, 200, 128, 8, 8, L, 0, 1, 0.1, 0.4),
+    ("experts_over_tokens", 2, 110, 128, 2048, 64, N, 0, 1, 0.0, 0.0),
+    ("ll_experts_over_tokens", 2, 100, 128, 1024, 40, L, QF, 1, 0.0, 0.0),
+]
+
+
+def buffers(p, w, total):
+    lay = ep.Layout(p)
+    recv = ep.Recv(p, total)
+    recv.x.view(torch.uint8).fill_(0x33)
+    if recv.scales is not None:
+        recv.scales.view(torch.uint8).fill_(0x33)
+    return lay, recv
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+def test_fused_equals_separate_calls_and_oracle(c):
+    name, R, T, H, E, K, mode, quant, align, mfrac, dfrac = c
+    say("fused", c)
+    w = inputs.small(f"fused_{name}", R=R, T=T, H=H, E=E, K=K, mode=mode, quant=quant, seed=97)
+    topk = inputs.gen_topk(w)
+    if mfrac or dfrac:
+        topk = inputs.masked_topk(w, topk, mfrac, dfrac, seed=4)
+    x = inputs.gen_x(w)
+    p = ep.Problem(R, T, H, E, K, align=align, mode=mode, quant=quant)
+    po = orc.Problem(R, T, H, E, K, align=align, mode=mode, quant=quant)
+    ol = orc.layout(po, topk)
+    cap = ep.max_recv_rows(p)
+    tk = torch.from_numpy(topk).to(DEV)
+    xg = torch.from_numpy(x).view(torch.bfloat16).to(DEV)
+    # fused
+    lf, rf = buffers(p, w, cap)
+    wsf = ep.workspace(p)
+    ep.dispatch_fused(p, tk, lf, xg, rf, wsf)
+    # separate
+    ls, rs = buffers(p, w, cap)
+    wss = ep.workspace(p)
+    ep.get_layout(p, tk, ls, wss)
+    ep.dispatch(p, ls, xg, recv=rs, ws=wss)
+    torch.cuda.synchronize()
+    for f in LAYOUT_FIELDS + ["err"]:
+        a, b = getattr(lf, f), getattr(ls, f)
+        if a is not None:
+            assert torch.equal(a, b), f
+    assert_layout_equal(lf, ol, mode)
+    if mode == N:
+        assert torch.equal(lf.recv_src_idx[: ol.total_rows], ls.recv_src_idx[: ol.total_rows])
+    sp = ol.send_pos[ol.send_pos >= 0]
+    rows = torch.from_numpy(np.unique(sp).astype(np.int64)).to(DEV)
+    assert torch.equal(rf.x[rows], rs.x[rows])
+    _, orecv, osc = orc.dispatch(po, x, topk, ol.send_pos, cap)
+    g = h(rf.x.view(torch.uint16) if quant == 0 else rf.x)
+    assert np.array_equal(g[rows.cpu().numpy()], orecv[rows.cpu().numpy()])
+    if quant:
+        assert torch.equal(rf.scales, rs.scales)
+
+
+@pytest.mark.parametrize("name", ["ll_decode", "normal_prefill"])
+def test_fused_workload(name):
+    """The low-latency decode and prefill shapes: every layout output against
+    the oracle and every dispatched row against the separate calls."""
+    w = inputs.WORKLOADS[name]
+    say("fused workload", name)
+    topk, x = inputs.gen_topk(w), inputs.gen_x(w)
+    p = ep.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+    po = orc.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+    ol = orc.layout(po, topk)
+    cap = ol.total_rows
+    tk = torch.from_numpy(topk).to(DEV)
+    xg = torch.from_numpy(x).view(torch.bfloat16).to(DEV)
+    lf = ep.Layout(p, recv_capacity=cap)
+    rf = ep.Recv(p, cap)
+    ep.dispatch_fused(p, tk, lf, xg, rf, ep.workspace(p))
+    torch.cuda.synchronize()
+    assert_layout_equal(lf, ol, w.mode)
+    ls = ep.Layout(p, recv_capacity=cap)
+    rs = ep.Recv(p, cap)
+    wss = ep.workspace(p)
+    ep.get_layout(p, tk, ls, wss)
+    ep.dispatch(p, ls, xg, recv=rs, ws=wss)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(np.unique(ol.send_pos[ol.send_pos >= 0]).astype(np.int64)).to(DEV)
+    step = 1 << 14
+    for a in range(0, rows.numel(), step):
+        r = rows[a:a + step]
+        assert torch.equal(rf.x[r], rs.x[r]), a
+    if w.quant:
+        G, RT = w.G, w.R * w.T
+        gi = torch.arange(G, device=DEV)
+        si = ((rows // RT)[:, None] * G + gi[None, :]) * RT + (rows % RT)[:, None]
+        assert torch.equal(rf.scales[si.reshape(-1)], rs.scales[si.reshape(-1)])
