@@ -6,9 +6,10 @@
 // recv_src_idx address book), sec. 3.2 (rank of an expert), sec. 4.3
 // (per-expert prefix sums as segment offsets).
 //
-// Up to 16K (token, k) entries: one launch (layout_direct, below).  Larger
-// problems take three launches, all small next to the data movement they
-// enable:
+// Small problems (up to a few thousand (token, k) entries, outside
+// rank-major mode): one launch (layout_direct, below).  Larger problems take
+// three launches, all small next to the data movement they enable (the
+// fused dispatch takes over the third):
 //   1. count   : one wavefront per token chunk.  Entries of a batch (one per
 //                lane, in (token, k) order) find their equal-key peers with
 //                one ballot per key bit; the lowest lane of each key advances
@@ -22,7 +23,8 @@
 //   3. finalize: every block scans the per-expert counts (rounded up to
 //                expert_alignment) into segment starts in LDS; slot = segment
 //                start + chunk prefix + rank in chunk; block 0 publishes the
-//                starts, rows per rank and row bases.
+//                starts, rows per rank and row bases.  Rank-major mode: slot
+//                = partition base + exclusive rank prefix + stream index.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 #include "layout_rows.hpp"
