@@ -18,19 +18,23 @@ from gpu_util import DEV, h, say
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # name, R, T, H, E, K, mode, quant
-    ("normal_bf16", 4, 40, 256, 16, 4, ep.MODE_NORMAL, ep.QUANT_NONE),
-    ("normal_ue8m0", 4, 40, 256, 16, 4, ep.MODE_NORMAL, ep.QUANT_FP8_UE8M0),
-    ("ll_fp8", 4, 24, 256, 8, 3, ep.MODE_LOW_LATENCY, ep.QUANT_FP8_F32),
-    ("ll_bf16", 2, 33, 128, 8, 2, ep.MODE_LOW_LATENCY, ep.QUANT_NONE),
-    ("messages_fp8", 4, 20, 256, 16, 4, ep.MODE_MESSAGES, ep.QUANT_FP8_F32),
+    # name, R, T, H, E, K, mode, quant, fused layout + dispatch
+    ("normal_bf16", 4, 40, 256, 16, 4, ep.MODE_NORMAL, ep.QUANT_NONE, False),
+    ("normal_ue8m0", 4, 40, 256, 16, 4, ep.MODE_NORMAL, ep.QUANT_FP8_UE8M0, False),
+    ("ll_fp8", 4, 24, 256, 8, 3, ep.MODE_LOW_LATENCY, ep.QUANT_FP8_F32, False),
+    ("ll_bf16", 2, 33, 128, 8, 2, ep.MODE_LOW_LATENCY, ep.QUANT_NONE, False),
+    ("messages_fp8", 4, 20, 256, 16, 4, ep.MODE_MESSAGES, ep.QUANT_FP8_F32, False),
+    ("rank_major_fp8", 4, 300, 256, 16, 4, ep.MODE_RANK_MAJOR, ep.QUANT_FP8_F32, False),
+    ("fused_normal_fp8", 4, 600, 256, 16, 4, ep.MODE_NORMAL, ep.QUANT_FP8_F32, True),
+    ("fused_ll_bf16", 4, 300, 128, 16, 8, ep.MODE_LOW_LATENCY, ep.QUANT_NONE, True),
 ]
 
 
 class Bufs:
     """One set of step buffers (inputs, handle, outputs)."""
 
-    def __init__(self, w, p):
+    def __init__(self, w, p, fused=False):
+        self.fused = fused
         self.topk = torch.zeros((w.R, w.T, w.K), dtype=torch.int32, device=DEV)
         self.x = torch.zeros((w.R, w.T, w.H), dtype=torch.bfloat16, device=DEV)
         self.wt = torch.zeros((w.R, w.T, w.K), dtype=torch.float32, device=DEV)
@@ -40,6 +44,10 @@ class Bufs:
         if w.mode == ep.MODE_MESSAGES:
             send_cap, desc_cap = ep.messages_capacity(p)  # worst case: no read-back
             self.msgs = ep.Messages(p, send_cap, desc_cap)
+            # delivery and the receiver, into the low-latency layout
+            self.arena = torch.empty(send_cap, dtype=torch.uint8, device=DEV)
+            self.unp = ep.unpack_buffers(p)
+            self.merr = torch.zeros(1, dtype=torch.int32, device=DEV)
         else:
             self.recv = ep.Recv(p, ep.max_recv_rows(p))
             self.out = torch.empty((w.R, w.T, w.H), dtype=torch.bfloat16, device=DEV)
@@ -63,17 +71,35 @@ class Bufs:
             if self.recv.scales is not None:
                 self.recv.scales.view(torch.uint8).fill_(0xA5)
             self.out.view(torch.int16).fill_(0x7F7F)
+        if self.recv is not None and self.recv.topk_idx is not None:
+            self.recv.topk_idx.fill_(-9)
+            self.recv.topk_weights.fill_(-9.0)
         if self.msgs is not None:
-            for t in (self.msgs.send_arena, self.msgs.descriptors):
+            for t in (self.msgs.send_arena, self.msgs.descriptors, self.arena):
                 t.fill_(0xA5)
             for t in (self.msgs.table, self.msgs.arena_base, self.msgs.num_descriptors):
                 t.fill_(-5)
+            self.unp[0].x.view(torch.uint8).fill_(0xA5)
+            self.unp[0].scales.view(torch.uint8).fill_(0xA5)
+            self.unp[1].fill_(-3)
+            self.unp[2].fill_(-1)
+            self.merr.zero_()
 
 
 def step(p, b: Bufs, y):
+    if b.fused:
+        ep.dispatch_fused(p, b.topk, b.lay, b.x, b.recv, b.ws)
+        ep.combine(p, b.lay, b.recv.x if y is None else y, b.wt, b.out)
+        return
     ep.get_layout(p, b.topk, b.lay, b.ws)
     if b.msgs is not None:
         ep.dispatch(p, b.lay, b.x, msgs=b.msgs, topk_idx=b.topk, topk_weights=b.wt, ws=b.ws)
+        ep.messages_execute(p, b.msgs, b.arena, b.merr)
+        ep.messages_unpack(p, b.msgs, b.arena, b.lay.num_tokens_per_expert, *b.unp, b.merr)
+        return
+    if p.mode == ep.MODE_RANK_MAJOR:
+        ep.dispatch(p, b.lay, b.x, recv=b.recv, topk_idx=b.topk, topk_weights=b.wt, ws=b.ws)
+        ep.combine(p, b.lay, b.recv.x if y is None else y, None, b.out)
         return
     ep.dispatch(p, b.lay, b.x, recv=b.recv, ws=b.ws)
     ep.combine(p, b.lay, b.recv.x if y is None else y, b.wt, b.out)
@@ -94,14 +120,22 @@ def compare(w, g: Bufs, e: Bufs):
         assert nd == int(h(e.msgs.num_descriptors)[0])
         assert torch.equal(g.msgs.descriptors[:nd], e.msgs.descriptors[:nd])
         ga, ea = h(g.msgs.send_arena), h(e.msgs.send_arena)
-        for off, reg in table.reshape(-1, 8)[:, [0, 2]]:
+        gr, er = h(g.arena), h(e.arena)
+        for off, roff, reg in table.reshape(-1, 8)[:, [0, 1, 2]]:
             if reg > 0:
                 assert np.array_equal(ga[off:off + reg], ea[off:off + reg])
+                assert np.array_equal(gr[roff:roff + reg], er[roff:roff + reg])
+        for a, b in zip((g.unp[0].x, g.unp[0].scales, g.unp[1], g.unp[2], g.merr),
+                        (e.unp[0].x, e.unp[0].scales, e.unp[1], e.unp[2], e.merr)):
+            assert torch.equal(a, b)
         return
     sp = h(g.lay.send_pos).reshape(-1)
     rows = torch.from_numpy(np.unique(sp[sp >= 0]).astype(np.int64)).to(DEV)
     assert torch.equal(g.lay.recv_src_idx[rows], e.lay.recv_src_idx[rows])
     assert torch.equal(g.recv.x[rows], e.recv.x[rows])
+    if g.recv.topk_idx is not None:
+        assert torch.equal(g.recv.topk_idx[rows], e.recv.topk_idx[rows])
+        assert torch.equal(g.recv.topk_weights[rows], e.recv.topk_weights[rows])
     if w.quant != ep.QUANT_NONE:
         G, RT, cap = w.G, w.R * w.T, g.recv.capacity
         gi = torch.arange(G, device=DEV)
@@ -116,11 +150,11 @@ def compare(w, g: Bufs, e: Bufs):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_graph_replay_matches_eager(case):
-    name, R, T, H, E, K, mode, quant = case
+    name, R, T, H, E, K, mode, quant, fused = case
     say("graph", name)
     w = inputs.small(f"graph_{name}", R=R, T=T, H=H, E=E, K=K, mode=mode, quant=quant, seed=31)
     p = ep.Problem(R, T, H, E, K, mode=mode, quant=quant, region_bytes=512, epoch=9)
-    cap_bufs, eager_bufs = Bufs(w, p), Bufs(w, p)
+    cap_bufs, eager_bufs = Bufs(w, p, fused), Bufs(w, p, fused)
     y = None
     if mode != ep.MODE_MESSAGES and quant != ep.QUANT_NONE:
         # bf16 expert outputs in the receive layout, fixed for every replay
@@ -156,3 +190,5 @@ def test_graph_replay_matches_eager(case):
         say("graph", name, "replay", rep)
         compare(w, cap_bufs, eager_bufs)
         assert int(h(cap_bufs.lay.err)[0]) == 0
+        if cap_bufs.msgs is not None:
+            assert int(h(cap_bufs.merr)[0]) == 0
