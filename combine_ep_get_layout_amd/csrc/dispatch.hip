@@ -267,9 +267,12 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
 // contiguously in a staging buffer (row-major, coalesced); this kernel
 // writes them column-major, scales[g * cap + row], a tile of consecutive
 // rows per group per store, through LDS.  Rows past the filled part of their
-// expert segment (alignment padding) are not written.  A scattered
-// per-row store of one byte per group would cost a memory transaction per
-// byte instead.
+// expert segment (alignment padding) are not written; with no padding
+// (expert_alignment 1, or rank-major) every staged row is filled and the
+// segment search is skipped.  A scattered per-row store of one byte per
+// group would cost a memory transaction per byte instead.  The tile is
+// read with 16-byte loads (tile_rows is a multiple of 16, so every tile
+// starts 16-byte aligned).
 template <int SB>
 __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restrict__ stage,
                                                          uint8_t* __restrict__ scales, int G,
@@ -281,27 +284,28 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
   extern __shared__ uint32_t lds[];
   int* starts = (int*)lds;                  // E + 1
   int* filled = starts + E + 1;             // tile_rows
-  uint32_t* tile = (uint32_t*)(filled + tile_rows);  // tile_rows * G * SB bytes
+  uint32_t* tile = lds + ((E + 1 + tile_rows + 3) & ~3);  // tile_rows * G * SB bytes, 16-aligned
   const int64_t total = min((int64_t)*row_base_end, limit);  // rows that were staged
   const int64_t r0 = (int64_t)blockIdx.x * tile_rows;
   if (r0 >= total) return;
   const int nrows = (int)min((int64_t)tile_rows, total - r0);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) starts[e] = expert_start[e];
-  if (threadIdx.x == 0) starts[E] = (int)total;
+  if (!all_filled) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) starts[e] = expert_start[e];
+    if (threadIdx.x == 0) starts[E] = (int)total;
+  }
   const int nbytes = nrows * G * SB;
   const uint8_t* src = stage + r0 * G * SB;
   uint8_t* t8 = (uint8_t*)tile;
-  if (SB == 4) {
-    for (int i = threadIdx.x; i < nbytes / 4; i += blockDim.x) tile[i] = ((const uint32_t*)src)[i];
-  } else {
-    for (int i = threadIdx.x; i < nbytes; i += blockDim.x) t8[i] = src[i];
-  }
+  const int nvec = nbytes / 16;
+  for (int i = threadIdx.x; i < nvec; i += blockDim.x)
+    ((u32x4*)tile)[i] = ((const u32x4*)src)[i];
+  for (int i = nvec * 16 + threadIdx.x; i < nbytes; i += blockDim.x) t8[i] = src[i];
   __syncthreads();
   for (int r = threadIdx.x; r < tile_rows; r += blockDim.x) {
     const int64_t row = r0 + r;
     int ok = 0;
     if (r < nrows && all_filled) {
-      ok = 1;  // rank-major: no padding rows
+      ok = 1;
     } else if (r < nrows) {
       int lo = 0, hi = E;  // last e with starts[e] <= row
       while (hi - lo > 1) {
@@ -376,23 +380,26 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
                        LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
                        a.err, row_meta(a), a.la);
   if (!LL) {
-    // 64 rows per tile, fewer for wide rows (the tile lives in LDS)
+    // 256 rows per tile, fewer for wide rows (the tile lives in LDS), at
+    // least 16 (16-byte aligned tiles)
     const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;
-    int tile_rows = 64;
-    while (tile_rows > 8 && (size_t)tile_rows * a.g.G * sb > 32768) tile_rows >>= 1;
-    const size_t lds = sizeof(int) * (a.g.E + 1 + tile_rows) + (size_t)tile_rows * a.g.G * sb + 16;
+    int tile_rows = 256;
+    while (tile_rows > 16 && (size_t)tile_rows * a.g.G * sb > 32768) tile_rows >>= 1;
+    const size_t lds = sizeof(int) * ((a.g.E + 1 + tile_rows + 3) & ~3) +
+                       (size_t)tile_rows * a.g.G * sb;
+    const int all_filled = RM || a.align == 1 ? 1 : 0;
     const int64_t tiles = (cap + tile_rows - 1) / tile_rows;
     if (tiles > 0) {
       if (Q == EP_QUANT_FP8_F32)
         hipLaunchKernelGGL(scales_to_columns<4>, dim3((unsigned)tiles), dim3(256), lds, st,
                            (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
                            a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
-                           tile_rows, RM ? 1 : 0);
+                           tile_rows, all_filled);
       else
         hipLaunchKernelGGL(scales_to_columns<1>, dim3((unsigned)tiles), dim3(256), lds, st,
                            (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
                            a.row_base + a.g.R, a.expert_start, a.recv_per_expert, a.g.E,
-                           tile_rows, RM ? 1 : 0);
+                           tile_rows, all_filled);
     }
   }
 }

@@ -236,6 +236,7 @@ int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layou
   a->stage = staged ? (char*)workspace + g.off_stage : nullptr;
   a->stage_rows = rank_major ? (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R)
                             : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+  a->align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;
   a->rank_major = rank_major;
   a->topk = rank_major ? topk_idx : nullptr;
   a->w = rank_major ? topk_weights : nullptr;

@@ -71,6 +71,7 @@ struct DispatchArgs {
   // segment starts / counts / row bases used to transpose it column-major
   void* stage;
   int64_t stage_rows;  // rows the staging buffer holds
+  int align;           // expert_alignment (normal mode; 1 otherwise)
   const int32_t* expert_start;
   const int32_t* recv_per_expert;
   const int32_t* row_base;

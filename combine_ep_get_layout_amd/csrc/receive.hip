@@ -225,13 +225,17 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
         const int64_t r = (int64_t)e * rt + pos;
         const u32x4* sv = (const u32x4*)(b + ms.off[0] + j * row_bytes);
         u32x4* dv = (u32x4*)((uint8_t*)a.recv_x + r * row_bytes);
-        // eight vectors per lane in flight; non-temporal stores keep the
-        // unpacked rows from displacing the caches (measured on MI355X: the
-        // next step's delivery runs 4.5% faster, the whole message step 2%)
+        // eight vectors per lane in flight; non-temporal loads and stores
+        // keep the message bodies and unpacked rows from displacing the
+        // caches.  Measured on MI355X: non-temporal stores make the next
+        // step's delivery 4.5% faster.  Non-temporal loads make the unpack
+        // 5.6% faster, and cut its HBM writes from 1.22 to 1.06 GB: the
+        // 4-byte column-major scale stores then stay in L2 until whole lines
+        // are written back.
         for (int v0 = lane; v0 < nvec; v0 += 8 * kWave) {
           u32x4 t[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) t[q] = sv[min(v0 + q * kWave, nvec - 1)];
+          for (int q = 0; q < 8; ++q) t[q] = __builtin_nontemporal_load(sv + min(v0 + q * kWave, nvec - 1));
 #pragma unroll
           for (int q = 0; q < 8; ++q)
             if (v0 + q * kWave < nvec) __builtin_nontemporal_store(t[q], dv + v0 + q * kWave);
