@@ -261,6 +261,8 @@ __global__ __launch_bounds__(256) void msg_pack_fp8(MessageArgs a, int P) {
     for (int i = 0; i < NP; ++i) {
       const int p = base + lane + kWave * i;
       if (p < P) {
+        // non-temporal (measured on MI355X: plain stores make the pack 4%
+        // faster and the next delivery 9% slower, as it writes them back)
         __builtin_nontemporal_store(cv[i], crow + p);
         if ((lane & 7) == 0) {
           const int64_t gi = (int64_t)j * g.G + (p >> 3);

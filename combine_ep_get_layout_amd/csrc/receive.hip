@@ -137,6 +137,12 @@ __global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
     set_err(a.err, bad);
     return;
   }
+  // a flag is 16 bytes at a 16-byte aligned offset (one vector); the byte
+  // loop covers any other last piece
+  if (p.len == 16 && ((p.src | p.dst) & 15) == 0) {
+    *(u32x4*)(a.recv + p.dst) = *(const u32x4*)(a.send + p.src);
+    return;
+  }
   for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
 }
 
