@@ -6,21 +6,28 @@ layout, and the combine gather-reduce back to token order.  The expert
 between dispatch and combine is the identity for bf16 layouts (combine
 reads the receive buffer), so the step moves exactly the path's own bytes;
 FP8 layouts combine bf16 expert outputs of the receive shape.  In message
-mode a step is the layout plus the packer (table, payload, header / flag /
-descriptors).
+mode a step is the layout, the packer (table, payload, header / flag /
+descriptors), the loopback delivery of the descriptors and the receiver
+that unpacks the delivered messages into the low-latency layout.
 
 The headline workload (`value`) is the normal-mode prefill shape: 8
 simulated ranks x 4096 tokens, hidden 7168 bf16, 256 experts, top-8 with
 Zipf(1.2) popularity, contiguous layout.  The other workloads of the method
 are timed alongside under "workloads": low-latency decode (8 x 128 tokens,
 packed masked, FP8 + fp32 scales), the FP8 training shape (16 x 8192,
-hidden 4096, UE8M0 column-major scales) and the 64-rank message packer.
+hidden 4096, UE8M0 column-major scales), the 64-rank message path, and the
+prefill routing in the rank-major (one row per token and destination rank)
+layout.
 
 `value` is algorithmic GB/s: the bytes the method must move (x read once,
 K receive rows written, K rows read back, the output written, plus the
 layout's index traffic) divided by the step time, with inputs resident in
-HBM before the timed region.  Per-phase times come from HIP events on the
-stream the library launches on (torch's current stream).
+HBM before the timed region.  Per-phase times (mean, median, p10, p90) come
+from a second pass with HIP events on the stream the library launches on
+(torch's current stream).  `without_layout` times the calls after the
+layout alone (dispatch + combine), the same way as the headline.
+Workloads whose data fit in the 256 MB last-level cache also report a
+cold-cache step time (`cold`: 1 GiB overwritten before every step).
 
 Prints one JSON line.  One GPU only: --gpus above 1 exits with a message.
 """
@@ -260,18 +267,57 @@ class Runner:
             raise RuntimeError(f"device error word {err}")
         names = [n for n, _ in self.phases()]
         ph = {k: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k in enumerate(names)}
-        return ms, {k: float(np.mean(v)) for k, v in ph.items()}, \
-            {k: float(np.median(v)) for k, v in ph.items()}
+        return ms, ph
 
-    def report(self, steps, warmup):
+    def run_without_layout(self, steps):
+        """The step's calls after the layout (dispatch and combine, or the
+        message calls), timed like the headline: the layout's outputs stay
+        valid since the routing does not change.  None when the layout is
+        fused into the dispatch."""
+        torch = self.torch
+        calls = [c for n, c in self.phases() if n != "layout"]
+        if len(calls) == len(self.phases()):
+            return None
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def run_cold(self, steps, flush_bytes=1 << 30):
+        """Step times with the last-level cache flushed before every step
+        (a 1 GiB buffer overwritten, untimed); events bracket each step."""
+        torch = self.torch
+        scratch = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(i)
+            evs[i][0].record()
+            self.step()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in evs]
+        del scratch
+        return t
+
+    def report(self, steps, warmup, extra=True):
         w = self.w
         log(f"[bench] {w.name}: timing {steps} steps after {warmup} warm-up")
-        ms, mean_ph, med_ph = self.run(steps, warmup)
+        ms, ph = self.run(steps, warmup)
+        mean_ph = {k: float(np.mean(v)) for k, v in ph.items()}
         total = sum(self.bytes.values())
-        phases = {k: {"ms_mean": round(mean_ph[k], 4), "ms_median": round(med_ph[k], 4),
+        phases = {k: {"ms_mean": round(mean_ph[k], 4),
+                      "ms_median": round(float(np.median(v)), 4),
+                      "ms_p10": round(float(np.percentile(v, 10)), 4),
+                      "ms_p90": round(float(np.percentile(v, 90)), 4),
                       "bytes": self.bytes[k],
                       "GBps": round(self.bytes[k] / (mean_ph[k] * 1e-3) / 1e9, 1)}
-                  for k in mean_ph}
+                  for k, v in ph.items()}
         dom = max(self.kernels, key=lambda k: mean_ph[k])
         kname = self.kernels[dom]
         ach = self.bytes[dom] / (mean_ph[dom] * 1e-3) / 1e9
@@ -294,9 +340,26 @@ class Runner:
                          "frac": round(ach / PEAK_HBM_GBPS, 4),
                          "traffic": traffic_from_profile(kname, w.name)},
         }
+        # the calls after the layout alone (the bar's dispatch + combine)
+        ms_nl = self.run_without_layout(steps) if extra else None
+        if ms_nl is not None:
+            b = total - self.bytes["layout"]
+            res["without_layout"] = {"calls": ", ".join(n for n in phases if n != "layout"),
+                                     "ms": round(ms_nl, 4),
+                                     "GBps": round(b / (ms_nl * 1e-3) / 1e9, 1),
+                                     "frac_of_peak": round(b / (ms_nl * 1e-3) / 1e9
+                                                           / PEAK_HBM_GBPS, 4)}
         res.update(self.extra)
         if total < 256e6:
             res["cache"] = "warm: the step's data fits in the 256 MB last-level cache"
+        if total < 256e6 and extra:
+            t = self.run_cold(steps)
+            med = float(np.median(t))
+            res["cold"] = {"note": "1 GiB overwritten before every step; events bracket each step",
+                           "ms_median": round(med, 4),
+                           "ms_p10": round(float(np.percentile(t, 10)), 4),
+                           "ms_p90": round(float(np.percentile(t, 90)), 4),
+                           "GBps": round(total / (med * 1e-3) / 1e9, 1)}
         return ms, res
 
 
@@ -320,10 +383,12 @@ def copy_probe(torch, nbytes=4 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, host, tokens_per_rank):
+def cpu_baseline(w, host, tokens_per_rank, min_seconds):
     """The plain C oracle on a bounded sample of the workload: the first
     `tokens_per_rank` tokens of every rank, layout + dispatch + combine,
-    single-threaded, outputs preallocated and touched before timing."""
+    single-threaded, outputs preallocated and touched before timing.  The
+    pass repeats until `min_seconds` have elapsed; the time per pass is
+    reported."""
     from oracle import oracle as orc
 
     topk, x, wt = host
@@ -337,15 +402,22 @@ def cpu_baseline(w, host, tokens_per_rank):
     recv = np.ones((rows, w.H), np.uint16)
     out = np.ones((w.R, T, w.H), np.uint16)
     t0 = time.perf_counter()
-    lay = orc.layout(p, topk)
-    orc.dispatch(p, x, topk, lay.send_pos, rows, out=(recv, None))
-    orc.combine(p, recv, wt, lay.send_pos, out=out)
-    dt = time.perf_counter() - t0
+    passes = 0
+    while True:
+        lay = orc.layout(p, topk)
+        orc.dispatch(p, x, topk, lay.send_pos, rows, out=(recv, None))
+        orc.combine(p, recv, wt, lay.send_pos, out=out)
+        passes += 1
+        total = time.perf_counter() - t0
+        if total >= min_seconds:
+            break
+    dt = total / passes
     sw = w.replace(T=T)
     nbytes = layout_bytes(sw, rows) + dispatch_bytes(sw) + combine_bytes(sw)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {T} of {w.T} tokens on each of the {w.R} ranks "
-                      f"(layout + dispatch + combine, {dt:.2f} s, single thread)",
+            "sample": f"first {T} of {w.T} tokens on each of the {w.R} ranks, layout + dispatch "
+                      f"+ combine, {passes} passes in {total:.1f} s ({dt:.2f} s per pass), "
+                      f"single thread",
             "tokens_per_s": round(w.R * T / dt, 1)}
 
 
@@ -357,10 +429,16 @@ def main():
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS),
                     help="comma-separated; the first is the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens per rank in the CPU-oracle sample (0 = all)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU-oracle pass repeats until this much time has elapsed")
     ap.add_argument("--fused", choices=["auto", "on", "off"], default="auto",
                     help="layout and dispatch in one call (ep_dispatch_fused): 'auto' uses it "
                          "for the workloads it measured faster on")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the without-layout and cold-cache passes (profiler runs, so "
+                         "every launch of a kernel is a warm launch of the timed step)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain copy of 2^30 bytes (counter calibration)")
     args = ap.parse_args()
@@ -383,7 +461,7 @@ def main():
         fused = args.fused == "on" or (args.fused == "auto" and name in FUSED_WORKLOADS)
         r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu), fused=fused)
         steps = args.steps if i == 0 else max(5, min(args.steps, 20))
-        ms, res = r.report(steps, args.warmup)
+        ms, res = r.report(steps, args.warmup, extra=not args.no_extra)
         if i == 0:
             head = (w, ms, res)
             if not args.no_cpu:
@@ -402,7 +480,7 @@ def main():
     probe = copy_probe(torch)
     w, ms, res = head
     if not args.no_cpu and w.mode != ep.MODE_MESSAGES:
-        cpu = cpu_baseline(w, host, min(args.cpu_tokens, w.T))
+        cpu = cpu_baseline(w, host, min(args.cpu_tokens or w.T, w.T), args.cpu_seconds)
 
     quant_dtype = {0: "bf16", 1: "fp8-e4m3+bf16", 2: "fp8-e4m3+bf16"}[w.quant]
     line = {
@@ -424,7 +502,9 @@ def main():
         "tokens_per_s": res["tokens_per_s"],
         "phases": res["phases"],
         "roofline": res["roofline"],
+        "without_layout": res.get("without_layout"),
         "copy_probe_GBps": round(probe, 1),
+        "frac_of_copy_probe": round(res["GBps"] / probe, 4),
         "workloads": others,
         "cpu_baseline": cpu,
     }
