@@ -403,12 +403,20 @@ def cpu_baseline(w, host, tokens_per_rank, min_seconds):
     out = np.ones((w.R, T, w.H), np.uint16)
     t0 = time.perf_counter()
     passes = 0
+    ph = {"layout": 0.0, "dispatch": 0.0, "combine": 0.0}
     while True:
+        ta = time.perf_counter()
         lay = orc.layout(p, topk)
+        tb = time.perf_counter()
         orc.dispatch(p, x, topk, lay.send_pos, rows, out=(recv, None))
+        tc = time.perf_counter()
         orc.combine(p, recv, wt, lay.send_pos, out=out)
+        td = time.perf_counter()
+        ph["layout"] += tb - ta
+        ph["dispatch"] += tc - tb
+        ph["combine"] += td - tc
         passes += 1
-        total = time.perf_counter() - t0
+        total = td - t0
         if total >= min_seconds:
             break
     dt = total / passes
@@ -418,7 +426,8 @@ def cpu_baseline(w, host, tokens_per_rank, min_seconds):
             "sample": f"first {T} of {w.T} tokens on each of the {w.R} ranks, layout + dispatch "
                       f"+ combine, {passes} passes in {total:.1f} s ({dt:.2f} s per pass), "
                       f"single thread",
-            "tokens_per_s": round(w.R * T / dt, 1)}
+            "tokens_per_s": round(w.R * T / dt, 1),
+            "phase_s": {k: round(v / passes, 4) for k, v in ph.items()}}
 
 
 def main():
