@@ -177,6 +177,58 @@ __global__ __launch_bounds__(1024) void dispatch_copy(const u32x4* __restrict__ 
   }
 }
 
+// LDS-staged copy (bf16, hidden up to 16384): one block of two wavefronts
+// per token.  The block loads the token's row into LDS once, then wave w
+// stores half w of the row (7 KiB contiguous at hidden 7168) to each of
+// the token's K rows, reading it back from LDS.  Measured on MI355X at the
+// prefill shape (8 x 4096 tokens, hidden 7168, top-8, Zipf routing): 2.6%
+// faster than the register-resident split above (four waves, 4 KiB each).
+// With four or eight waves, the same LDS-staged scheme is 3-5% slower than
+// the register split. So is one wave per destination row. Register splits
+// of two waves (7 KiB each) are 2% slower.
+template <bool RM, bool FU>
+__global__ __launch_bounds__(128) void dispatch_copy_lds(const u32x4* __restrict__ x,
+                                                         const int32_t* __restrict__ send_pos,
+                                                         u32x4* __restrict__ recv, int V, int K,
+                                                         int64_t cap, int32_t* err, RowMeta meta,
+                                                         LayoutArgs la) {
+  extern __shared__ u32x4 row_lds[];  // V vectors
+  __shared__ int start[FU ? 2049 : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int tok = blockIdx.x;
+  if (FU) {
+    if (la.mode != EP_MODE_LOW_LATENCY) segment_starts(la, start);
+    fused_publish(la, start);
+    if (tok >= la.g.R * la.g.T) return;  // publishing-only block
+  }
+  const u32x4* src = x + (int64_t)tok * V;
+  for (int j = threadIdx.x; j < V; j += blockDim.x) row_lds[j] = src[j];
+  const int myrow = FU ? fused_token_rows(la, tok, wave == 0, start)
+                       : (lane < K ? send_pos[(int64_t)tok * K + lane] : -1);
+  // rank-major: each destination row once; wave 0 writes its metadata
+  const uint64_t keep = RM ? first_of_rows(myrow, K) : ~0ull;
+  const bool meta_wave = RM && wave == 0 && (meta.idx || meta.wts);
+  const int myid = meta_wave && lane < K ? meta.topk[(int64_t)tok * K + lane] : -1;
+  const float myw = meta_wave && meta.wts && lane < K ? meta.w[(int64_t)tok * K + lane] : 0.0f;
+  __syncthreads();
+  const int half = (V + 1) / 2;
+  const int lo = wave * half, hi = min(V, lo + half);
+  for (int k = 0; k < K; ++k) {
+    if (RM && !((keep >> k) & 1)) continue;
+    const int row = __builtin_amdgcn_readlane(myrow, k);
+    if (row < 0) continue;
+    if (row >= cap) {
+      if (lane == 0 && wave == 0) set_err(err, EP_DEVERR_CAPACITY);
+      continue;
+    }
+    if (meta_wave)
+      write_row_meta(meta, K, row, __builtin_amdgcn_readlane(myid, k) / meta.L, myid, myw);
+    u32x4* dst = recv + (int64_t)row * V;
+    for (int j = lo + lane; j < hi; j += kWave) dst[j] = row_lds[j];
+  }
+}
+
 // P = 16-channel pairs per row (H / 16); a group of 128 channels is 8
 // pairs = 8 consecutive lanes, reduced with DPP.
 // Work-groups are dealt to the kXcds dies round-robin (block b on die
@@ -362,6 +414,23 @@ static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t 
                        row_meta(a), a.la);
 }
 
+// LDS-staged bf16 copy up to hidden 16384 (32 KiB of LDS per block)
+constexpr int kCopyLdsMaxVectors = 2048;
+
+template <bool RM>
+static void launch_copy_lds(const DispatchArgs& a, int V, hipStream_t st) {
+  const int N = a.g.R * a.g.T;
+  const size_t lds = sizeof(u32x4) * (size_t)V;
+  if (a.fused)
+    hipLaunchKernelGGL((dispatch_copy_lds<false, true>), dim3(fused_blocks(a, N)), dim3(128), lds,
+                       st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
+                       row_meta(a), a.la);
+  else
+    hipLaunchKernelGGL((dispatch_copy_lds<RM, false>), dim3(N), dim3(128), lds, st,
+                       (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
+                       row_meta(a), a.la);
+}
+
 template <int NP, int Q, bool LL, bool RM>
 static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t st) {
   const int N = a.g.R * a.g.T;
@@ -429,9 +498,14 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   if (N == 0) return hipSuccess;
   if (a.quant == EP_QUANT_NONE) {
     const int V = a.g.H / 8;
-    const RowSplit rs = row_split(V, 4);  // hidden <= 32768: nv = 4, <= 16 waves
-    if (a.rank_major) launch_copy_nv<4, true>(a, V, rs.waves, st);
-    else launch_copy_nv<4, false>(a, V, rs.waves, st);
+    if (V <= kCopyLdsMaxVectors) {
+      if (a.rank_major) launch_copy_lds<true>(a, V, st);
+      else launch_copy_lds<false>(a, V, st);
+    } else {
+      const RowSplit rs = row_split(V, 4);  // hidden <= 32768: nv = 4, <= 16 waves
+      if (a.rank_major) launch_copy_nv<4, true>(a, V, rs.waves, st);
+      else launch_copy_nv<4, false>(a, V, rs.waves, st);
+    }
   } else if (a.quant == EP_QUANT_FP8_F32) {
     launch_fp8_mode<EP_QUANT_FP8_F32>(a, st);
   } else {

@@ -35,6 +35,9 @@ SMALL = [
     ("r64", 64, 40, 128, 256, 8, 1, N, QN, 0.0, 0.0, 0),
     ("e_eq_r", 8, 300, 128, 8, 4, 1, N, QN, 0.0, 0.5, 0),
     ("h_tail", 2, 16, 7176, 8, 2, 1, N, QN, 0.0, 0.0, 0),
+    ("h_16k_lds", 2, 9, 16384, 8, 3, 1, N, QN, 0.1, 0.0, 0),  # widest LDS-staged copy
+    ("h_32k_regs", 2, 7, 32768, 8, 3, 2, N, QN, 0.1, 0.1, 0),  # register-resident copy
+    ("ll_h_16392", 2, 5, 16392, 4, 2, 1, LL, QN, 0.0, 0.3, 0),
     ("ll", 4, 130, 256, 16, 4, 1, LL, QN, 0.1, 0.0, 0),
     ("ll_dup", 2, 20, 128, 4, 4, 1, LL, QN, 0.0, 0.9, 0),
     ("fp8n", 4, 333, 384, 16, 4, 1, N, QF, 0.05, 0.0, 0),

@@ -24,6 +24,7 @@ FIXED = [
     ("r8_chunks", 8, 700, 128, 64, 6, ep.QUANT_NONE, 0.05, 0.1),
     ("r5_odd", 5, 130, 384, 10, 5, ep.QUANT_FP8_F32, 0.2, 0.0),
     ("r16_wide", 16, 64, 1024, 256, 8, ep.QUANT_NONE, 0.0, 0.0),
+    ("r2_h20480", 2, 9, 20480, 4, 2, ep.QUANT_NONE, 0.1, 0.2),  # register-resident copy
     ("r3_empty", 3, 0, 128, 6, 2, ep.QUANT_NONE, 0.0, 0.0),
 ]
 
