@@ -88,8 +88,9 @@ def combine_bytes(w, rows=None):
 # sources each profiled kernel is built from (its counters go stale when
 # any of them changes)
 KERNEL_SOURCES = {
-    "dispatch_copy": ["dispatch.hip", "ep_device.hpp", "ep_internal.hpp"],
-    "dispatch_fp8": ["dispatch.hip", "quant.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "dispatch_copy": ["dispatch.hip", "layout_rows.hpp", "ep_device.hpp", "ep_internal.hpp"],
+    "dispatch_fp8": ["dispatch.hip", "layout_rows.hpp", "quant.hpp", "ep_device.hpp",
+                     "ep_internal.hpp"],
     "combine_rows": ["combine.hip", "ep_device.hpp", "ep_internal.hpp"],
     "msg_pack_fp8": ["messages.hip", "msg_format.hpp", "quant.hpp", "ep_device.hpp",
                      "ep_internal.hpp"],
