@@ -156,6 +156,10 @@ __global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
 // back as partial lines from eight L2s.
 constexpr int kXcds = 8;
 
+constexpr int kUnpackSeg = 2048;   // entries ranked per round (LDS slots)
+constexpr int kUnpackMaxL = 2048;  // local experts (E <= 2048)
+constexpr int kUnpackWaves = 8;
+
 __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   const Geometry& g = a.g;
   const int R = g.R, L = g.L, E = g.E, K = g.K, H = g.H, G = g.G, T = g.T;
@@ -205,20 +209,48 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   const int64_t row_bytes = (int64_t)H * cb;
   const int nvec = (int)(row_bytes / 16);
   const int64_t nent = n * K;
-  for (int l = wave; l < L; l += nw) {
-    const int e = d * L + l;
-    int64_t run = 0;  // slots taken by earlier sources
-    for (int s2 = lane; s2 < s; s2 += kWave) run += a.cnt_expert[(int64_t)s2 * E + e];
-    for (int o = 32; o > 0; o >>= 1) run += __shfl_xor(run, o);
-    for (int64_t i0 = 0; i0 < nent; i0 += kWave) {
-      const int64_t i = i0 + lane;
-      const int id = i < nent ? ids[i] : -1;
-      uint64_t hits = __ballot(id == e);
-      while (hits) {  // in (token, k) order
+  // Slots, in segments of kUnpackSeg entries.  Phase 1: wavefront w ranks
+  // the entries of local experts w, w + nw, ... by ballot, in (token, k)
+  // order, continuing each expert's count from the earlier segments
+  // (run[l], LDS), and records every entry's slot (-1: not on d).  Phase 2:
+  // the segment's entries are dealt to the wavefronts in tiles of 64, and
+  // each wavefront copies the rows, scales and source index of its tiles'
+  // hits, so an expert that draws most of a message's entries does not
+  // leave the other wavefronts idle.
+  __shared__ int slot[kUnpackSeg];
+  __shared__ int run[kUnpackMaxL];
+  for (int l = wave; l < L; l += nw) {  // slots taken by earlier sources
+    int64_t r = 0;
+    for (int s2 = lane; s2 < s; s2 += kWave) r += a.cnt_expert[(int64_t)s2 * E + d * L + l];
+    for (int o = 32; o > 0; o >>= 1) r += __shfl_xor(r, o);
+    if (lane == 0) run[l] = (int)r;
+  }
+  for (int64_t seg0 = 0; seg0 < nent; seg0 += kUnpackSeg) {
+    const int nseg = (int)min((int64_t)kUnpackSeg, nent - seg0);
+    for (int i = threadIdx.x; i < nseg; i += blockDim.x) slot[i] = -1;
+    __syncthreads();
+    for (int l = wave; l < L; l += nw) {
+      const int e = d * L + l;
+      int r = run[l];
+      for (int i0 = 0; i0 < nseg; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool hit = i < nseg && ids[seg0 + i] == e;
+        const uint64_t hits = __ballot(hit);
+        if (hit) slot[i] = r + (int)__popcll(hits & lanes_below());
+        r += (int)__popcll(hits);
+      }
+      if (lane == 0) run[l] = r;
+    }
+    __syncthreads();
+    for (int i0 = wave * kWave; i0 < nseg; i0 += nw * kWave) {
+      const int myslot = i0 + lane < nseg ? slot[i0 + lane] : -1;
+      uint64_t hits = __ballot(myslot >= 0);
+      while (hits) {  // in (token, k) order within the tile
         const int hl = __builtin_ctzll(hits);
         hits &= hits - 1;
-        const int64_t j = (i0 + hl) / K;
-        const int64_t pos = run++;
+        const int64_t i = seg0 + i0 + hl;
+        const int64_t j = i / K;
+        const int64_t pos = __builtin_amdgcn_readlane(myslot, hl);
         if (pos >= rt) {
           if (lane == 0) set_err(a.err, EP_DEVERR_LL_OVERFLOW);
           continue;
@@ -228,6 +260,7 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
           if (lane == 0) set_err(a.err, EP_DEVERR_MESSAGE);
           continue;
         }
+        const int e = ids[i];
         const int64_t r = (int64_t)e * rt + pos;
         const u32x4* sv = (const u32x4*)(b + ms.off[0] + j * row_bytes);
         u32x4* dv = (u32x4*)((uint8_t*)a.recv_x + r * row_bytes);
@@ -239,12 +272,13 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
         // 4-byte column-major scale stores then stay in L2 until whole lines
         // are written back.
         for (int v0 = lane; v0 < nvec; v0 += 8 * kWave) {
-          u32x4 t[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) t[q] = __builtin_nontemporal_load(sv + min(v0 + q * kWave, nvec - 1));
+          u32x4 tv[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            if (v0 + q * kWave < nvec) __builtin_nontemporal_store(t[q], dv + v0 + q * kWave);
+            tv[q] = __builtin_nontemporal_load(sv + min(v0 + q * kWave, nvec - 1));
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (v0 + q * kWave < nvec) __builtin_nontemporal_store(tv[q], dv + v0 + q * kWave);
         }
         if (sb == 4) {
           const float* ss = (const float*)(b + ms.off[1]) + j * G;
@@ -258,6 +292,7 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
         if (lane == 0) a.recv_src_idx[r] = (int32_t)((int64_t)s * T + t);
       }
     }
+    __syncthreads();  // slot[] is reused by the next segment
   }
 }
 
@@ -279,7 +314,7 @@ hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
 
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st) {
   const int R = a.g.R;
-  int waves = a.g.L < 16 ? a.g.L : 16;
+  const int waves = kUnpackWaves;
   const unsigned blocks = (unsigned)(kXcds * ((R + kXcds - 1) / kXcds) * R);  // (d, s) pairs
   hipLaunchKernelGGL(msg_unpack, dim3(blocks), dim3(kWave * waves), 0, st, a);
   return hipGetLastError();
