@@ -412,6 +412,7 @@ int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t*
   a.arena = recv_arena;
   a.recv_cap = recv_capacity;
   a.table = m->table;
+  a.arena_base = aligned(m->arena_base, 8) ? m->arena_base : nullptr;
   a.cnt_expert = num_tokens_per_expert;
   a.recv_x = out->x;
   a.recv_scales = out->scales;

@@ -153,6 +153,7 @@ struct UnpackArgs {
   const uint8_t* arena;        // receive arenas
   int64_t recv_cap;
   const int64_t* table;        // [R][R][8]
+  const int64_t* arena_base;   // [2][R+1] or NULL (receive loads, for the block order)
   const int32_t* cnt_expert;   // [R][E]
   void* recv_x;                // [E*R*T][H] bf16 or codes
   void* recv_scales;           // [E][G][R*T]

@@ -159,12 +159,39 @@ constexpr int kXcds = 8;
 constexpr int kUnpackSeg = 2048;   // entries ranked per round (LDS slots)
 constexpr int kUnpackMaxL = 2048;  // local experts (E <= 2048)
 constexpr int kUnpackWaves = 8;
+constexpr int kUnpackChunk = 16;   // sources per die run under skewed loads
 
 __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   const Geometry& g = a.g;
   const int R = g.R, L = g.L, E = g.E, K = g.K, H = g.H, G = g.G, T = g.T;
-  const int x = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
-  const int d = x + kXcds * (rest / R), s = rest % R;
+  // Block -> (destination d, source s).  Balanced receive loads: each
+  // destination's messages run on one die, in source order (the dies take
+  // destinations round-robin).  Skewed loads (one destination receiving
+  // more than twice the mean bytes, from the receive-arena bases) would
+  // overload that die, so there the dies take runs of kUnpackChunk
+  // sources of every destination instead.  Every block takes the same
+  // decision, so the mapping stays a bijection.
+  bool skewed = false;
+  if (a.arena_base && R >= 2 * kUnpackChunk) {
+    const int64_t* rb = a.arena_base + R + 1;
+    int64_t mx = 0;
+    for (int q = lane_id(); q < R; q += kWave) mx = max(mx, rb[q + 1] - rb[q]);
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (int64_t)__shfl_xor(mx, o));
+    skewed = mx * R > 2 * rb[R];
+  }
+  int d, s;
+  if (!skewed) {
+    const int x = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+    d = x + kXcds * (rest / R);
+    s = rest % R;
+  } else {
+    const int nch = (R + kUnpackChunk - 1) / kUnpackChunk;
+    const int x = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
+    const int q = x + kXcds * (m / kUnpackChunk);
+    d = q / nch;
+    s = (q % nch) * kUnpackChunk + m % kUnpackChunk;
+    if (s >= R) return;
+  }
   if (d >= R) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int64_t rt = (int64_t)R * T;
@@ -315,7 +342,11 @@ hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st) {
   const int R = a.g.R;
   const int waves = kUnpackWaves;
-  const unsigned blocks = (unsigned)(kXcds * ((R + kXcds - 1) / kXcds) * R);  // (d, s) pairs
+  // enough blocks for either mapping of (d, s) pairs
+  const int nch = (R + kUnpackChunk - 1) / kUnpackChunk;
+  const int64_t by_dest = (int64_t)kXcds * ((R + kXcds - 1) / kXcds) * R;
+  const int64_t by_chunk = (int64_t)kXcds * ((R * nch + kXcds - 1) / kXcds) * kUnpackChunk;
+  const unsigned blocks = (unsigned)(by_dest > by_chunk ? by_dest : by_chunk);
   hipLaunchKernelGGL(msg_unpack, dim3(blocks), dim3(kWave * waves), 0, st, a);
   return hipGetLastError();
 }

@@ -78,10 +78,14 @@ def compare_unpacked(w, out, cnt, src, u):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_execute_and_unpack_match_oracle(case):
+    check_case(case)
+
+
+def check_case(case, **kw):
     name, R, T, H, E, K, quant, rb, mfrac, dfrac = case
     say("receive", name)
     w = inputs.small(f"recv_{name}", R=R, T=T, H=H, E=E, K=K, mode=ep.MODE_MESSAGES, quant=quant,
-                     seed=61, region_bytes=rb, epoch=5)
+                     seed=61, region_bytes=rb, epoch=5, **kw)
     topk = inputs.gen_topk(w)
     if mfrac or dfrac:
         topk = inputs.masked_topk(w, topk, mfrac, dfrac, seed=3)
@@ -106,6 +110,20 @@ def test_execute_and_unpack_match_oracle(case):
     assert torch.equal(src[rows], ll.recv_src_idx[rows])
     assert torch.equal(cnt, ll.recv_tokens_per_expert)
     assert int(h(ll.err)[0]) == int(h(err)[0])
+    return h(msgs.arena_base)
+
+
+@pytest.mark.parametrize("alpha,skewed", [(None, False), (2.5, True)], ids=["uniform", "zipf"])
+def test_unpack_block_orders_32_ranks(alpha, skewed):
+    """32 ranks: the receiver's block order follows the receive loads (one
+    die per destination when balanced, runs of 16 sources per die when one
+    destination receives more than twice the mean); both orders give the
+    oracle's bytes."""
+    kw = {} if alpha is None else {"routing": "zipf", "alpha": alpha}
+    base = check_case((f"r32_{'zipf' if alpha else 'uniform'}", 32, 24, 256, 64, 4,
+                       ep.QUANT_FP8_F32, 2048, 0.0, 0.0), **kw)
+    sizes = np.diff(base[1])
+    assert (sizes.max() * 32 > 2 * base[1][-1]) == skewed
 
 
 def test_unpack_rejects_corrupt_flag_and_header_like_the_oracle():
