@@ -265,8 +265,10 @@ int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv
  * filled are left as they were.  pos >= R*T sets EP_DEVERR_LL_OVERFLOW; a
  * message past recv_capacity sets EP_DEVERR_CAPACITY; errors are OR-ed into
  * *err.  out->capacity >= E*R*T; recv_src_idx: [E*R*T]; recv_count: [E];
- * num_tokens_per_expert: [R][E] (ep_get_layout's).  p->mode must be
- * EP_MODE_MESSAGES (p->quant, p->epoch describe the messages). */
+ * num_tokens_per_expert: [R][E] (ep_get_layout's).  m->arena_base, when
+ * not NULL, only chooses the block order from the receive loads (results
+ * are the same either way).  p->mode must be EP_MODE_MESSAGES (p->quant,
+ * p->epoch describe the messages). */
 int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t* recv_arena,
                        int64_t recv_capacity, const int32_t* num_tokens_per_expert,
                        const ep_recv* out, int32_t* recv_count, int32_t* recv_src_idx,
