@@ -330,6 +330,7 @@ class Runner:
                   for k, v in ph.items()}
         dom = max(self.kernels, key=lambda k: mean_ph[k])
         kname = self.kernels[dom]
+        traffic = traffic_from_profile(kname, w.name)
         ach = self.bytes[dom] / (mean_ph[dom] * 1e-3) / 1e9
         mode = {0: "contiguous", 1: "packed-masked", 2: "messages", 3: "rank-major"}[w.mode]
         payload = {0: "bf16", 1: "fp8-e4m3 fp32 scales", 2: "fp8-e4m3 ue8m0 scales"}[w.quant]
@@ -348,8 +349,10 @@ class Runner:
             "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1),
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_GBPS, 4),
-                         "traffic": traffic_from_profile(kname, w.name)},
+                         "traffic": traffic},
         }
+        if traffic is not None:  # counted HBM bytes over the same launch time
+            res["roofline"]["traffic_GBps"] = round(traffic / (mean_ph[dom] * 1e-3) / 1e9, 1)
         # the calls after the layout alone (the bar's dispatch + combine)
         ms_nl = self.run_without_layout(steps) if extra else None
         if ms_nl is not None:
