@@ -7,13 +7,15 @@
 // packed masked layout; fp32 or power-of-two scales, column-major), sec. 4.6
 // (these kernels move bytes and do no matrix math: HBM is the roof).
 //
-// Work split: one block per token, one wavefront per piece of the row, so
-// the whole row is in flight at once.  Each wave reads its piece once into
-// registers (16-byte loads, fully coalesced), quantises it once if asked,
-// and stores it to each of the token's K rows with 16-byte stores.  The
-// source row is read once, not K times.  (Measured on MI355X at hidden
-// 7168: plain stores beat non-temporal ones for this scatter; the kernel
-// sits at the chip's write-dominated bandwidth.)
+// Work split: one block per token; the source row is read once, not K
+// times, and stored to each of the token's K rows with 16-byte stores.
+//  - bf16 up to hidden 16384: the row is staged in LDS and two wavefronts
+//    each store half of every destination row (dispatch_copy_lds);
+//  - wider bf16 rows, and FP8: one wavefront per piece of the row, held in
+//    registers (quantised once if asked), the whole row in flight at once.
+// (Measured on MI355X at hidden 7168: plain stores beat non-temporal ones
+// for this scatter; the kernel sits at the chip's write-dominated
+// bandwidth.)
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 #include "layout_rows.hpp"

@@ -18,13 +18,14 @@
 //      copies with 16-byte vectors, four per thread in flight;
 //   2. one thread per message copies its flag.
 //   The launch boundary puts every payload and header before every flag.
-// Unpack, one launch: one block per (source, destination) message, one
-// wavefront per local expert of the destination.  Thread 0 checks the
-// header and the flag once (no waiting: a message that fails is reported
-// and skipped).  The wavefront walks the message's expert ids in (token, k)
-// order with one ballot per 64 entries; each match takes the next slot of
-// its expert after the slots of earlier sources, and the wavefront copies
-// the token's row and scales there.
+// Unpack, one launch: one block of eight wavefronts per (source,
+// destination) message.  Thread 0 checks the header and the flag once (no
+// waiting: a message that fails is reported and skipped).  The message's
+// entries are taken in segments: the wavefronts first rank the segment's
+// expert ids, one local expert each, with one ballot per 64 entries (each
+// match takes the next slot of its expert after the slots of earlier
+// sources and segments); then all eight copy the matched tokens' rows and
+// scales to their slots, 64 entries at a time each.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 #include "msg_format.hpp"
