@@ -446,7 +446,7 @@ def cpu_baseline(w, host, tokens_per_rank, min_seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS),
                     help="comma-separated; the first is the headline")
@@ -482,7 +482,7 @@ def main():
         w = inputs.WORKLOADS[name]
         fused = args.fused == "on" or (args.fused == "auto" and name in FUSED_WORKLOADS)
         r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu), fused=fused)
-        steps = args.steps if i == 0 else max(5, min(args.steps, 20))
+        steps = args.steps if i == 0 else max(5, min(args.steps, 50))
         ms, res = r.report(steps, args.warmup, extra=not args.no_extra)
         if i == 0:
             head = (w, ms, res)
