@@ -46,10 +46,19 @@ SMALL = [
     ("ue8ll", 2, 64, 128, 8, 2, 1, LL, QU, 0.0, 0.0, 0),
     ("fp8_htail", 2, 16, 8320, 8, 2, 1, LL, QF, 0.0, 0.0, 0),
     ("empty", 2, 0, 128, 8, 2, 1, N, QN, 0.0, 0.0, 0),
+    # the documented limits: 256 ranks, 2048 experts, top-64, hidden 32768
+    ("max_r", 256, 3, 128, 256, 8, 1, N, QN, 0.1, 0.1, 0),
+    ("max_r_chunked", 256, 5, 128, 512, 8, 2, N, QN, 0.05, 0.0, 0),
+    ("max_e_k", 4, 9, 128, 2048, 64, 2, N, QN, 0.05, 0.1, 0),
+    ("max_k_ll", 2, 16, 128, 64, 64, 1, LL, QN, 0.0, 0.0, 0),
+    ("max_r_ll", 256, 2, 128, 256, 4, 1, LL, QF, 0.0, 0.0, 0),
+    ("max_h_fp8", 2, 5, 32768, 8, 2, 1, N, QF, 0.0, 0.0, 0),
+    ("max_h_ue8_ll", 2, 3, 32768, 4, 2, 1, LL, QU, 0.0, 0.0, 0),
     ("msg", 4, 50, 256, 16, 4, 1, MSG, QF, 0.1, 0.1, 512),
     ("msg_ue8", 3, 40, 128, 6, 3, 1, MSG, QU, 0.0, 0.0, 256),
     ("msg_bf16", 4, 30, 136, 8, 3, 1, MSG, QN, 0.1, 0.0, 128),
     ("msg_r64", 64, 12, 256, 128, 8, 1, MSG, QF, 0.0, 0.0, 4096),
+    ("msg_max_r", 256, 2, 128, 256, 4, 1, MSG, QF, 0.0, 0.0, 4096),
 ]
 IDS = [c[0] for c in SMALL]
 

@@ -29,6 +29,7 @@ CASES = [
     ("r8_wide", 8, 40, 1024, 64, 8, ep.QUANT_FP8_F32, 8192, 0.05, 0.0),
     ("r16_many_local", 16, 24, 256, 512, 6, ep.QUANT_FP8_F32, 1024, 0.0, 0.0),
     ("r4_bf16_dups", 4, 33, 128, 8, 8, ep.QUANT_NONE, 128, 0.1, 0.4),
+    ("r256", 256, 2, 128, 256, 4, ep.QUANT_FP8_F32, 4096, 0.0, 0.0),  # the rank limit
 ]
 FILL = 0x5C
 
