@@ -486,6 +486,15 @@ static void launch_fp8_q(const DispatchArgs& a, hipStream_t st) {
   const int P = a.g.H / 16;
   RowSplit rs = row_split(P, 1);
   if (rs.nv >= 3) rs = RowSplit{4, ((P + kWave * 4 - 1) / (kWave * 4) + 3) / 4 * 4};  // <= 8 waves
+  // Normal and rank-major modes, one wavefront per token where measured
+  // faster on MI355X (training routing, interleaved runs):
+  //  - up to 64 pairs (hidden 1024): one pair per lane, 24% faster than four
+  //    wavefronts of which three are idle;
+  //  - 256 pairs (hidden 4096): four pairs per lane, 0.6-1.2% faster than
+  //    four wavefronts of one pair each.
+  // At 128 and 192 pairs one wavefront was 2-5% slower, so those keep the
+  // split above.
+  if (!LL && (P <= kWave || P == kWave * 4)) rs = RowSplit{(P + kWave - 1) / kWave, 1};
   switch (rs.nv) {
     case 1: launch_fp8_np<1, Q, LL, RM>(a, P, rs.waves, st); break;
     case 2: launch_fp8_np<2, Q, LL, RM>(a, P, rs.waves, st); break;

@@ -53,6 +53,8 @@ SMALL = [
     ("max_k_ll", 2, 16, 128, 64, 64, 1, LL, QN, 0.0, 0.0, 0),
     ("max_r_ll", 256, 2, 128, 256, 4, 1, LL, QF, 0.0, 0.0, 0),
     ("max_h_fp8", 2, 5, 32768, 8, 2, 1, N, QF, 0.0, 0.0, 0),
+    ("fp8_h4096_one_wave", 4, 37, 4096, 16, 4, 2, N, QU, 0.1, 0.1, 0),
+    ("fp8_h2048", 3, 21, 2048, 12, 3, 1, N, QF, 0.05, 0.0, 0),
     ("max_h_ue8_ll", 2, 3, 32768, 4, 2, 1, LL, QU, 0.0, 0.0, 0),
     ("msg", 4, 50, 256, 16, 4, 1, MSG, QF, 0.1, 0.1, 512),
     ("msg_ue8", 3, 40, 128, 6, 3, 1, MSG, QU, 0.0, 0.0, 256),

@@ -26,6 +26,7 @@ FIXED = [
     ("r16_wide", 16, 64, 1024, 256, 8, ep.QUANT_NONE, 0.0, 0.0),
     ("r2_h20480", 2, 9, 20480, 4, 2, ep.QUANT_NONE, 0.1, 0.2),  # register-resident copy
     ("r256", 256, 3, 128, 256, 8, ep.QUANT_NONE, 0.1, 0.1),  # the rank limit
+    ("r4_h4096_fp8", 4, 30, 4096, 16, 4, ep.QUANT_FP8_UE8M0, 0.1, 0.2),
     ("r4_e2048_k64", 4, 9, 256, 2048, 64, ep.QUANT_FP8_F32, 0.05, 0.1),  # expert and top-k limits
     ("r3_empty", 3, 0, 128, 6, 2, ep.QUANT_NONE, 0.0, 0.0),
 ]
