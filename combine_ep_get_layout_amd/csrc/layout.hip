@@ -560,8 +560,12 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   hipError_t e = launch_layout_counts(a, stream);
   if (e != hipSuccess) return e;
   const int64_t work = (int64_t)g.R * g.T * (g.K > g.R ? g.K : g.R);
+  // a thread per item, at most 1024 blocks: every block first scans the
+  // segment starts, so past that more items per thread are cheaper than
+  // more blocks (measured on MI355X: the 64-rank message layout is 3.7 us
+  // faster with 1024 blocks of four items per thread than with 4096)
   int64_t fb = (work + 255) / 256;
-  if (fb > 4096) fb = 4096;
+  if (fb > 1024) fb = 1024;
   if (fb < 1) fb = 1;
   hipLaunchKernelGGL(layout_finalize, dim3((unsigned)fb), dim3(256), 0, stream, a);
   return hipGetLastError();
