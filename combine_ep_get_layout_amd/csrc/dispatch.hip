@@ -29,8 +29,10 @@ namespace ep {
 // is rounded up to a multiple of four, one per SIMD of a compute unit.
 // Measured on MI355X at hidden 7168 (whole library, alternating runs): the
 // FP8 low-latency dispatch with eight waves, one idle, is 2% faster than
-// with seven; the bf16 copy with four waves of four vectors is 1.4% faster
-// than eight waves of two and 1.7% faster than seven waves of two.
+// with seven; the register bf16 copy (used above hidden 16384) with four
+// waves of four vectors is 1.4% faster than eight waves of two and 1.7%
+// faster than seven waves of two.  The FP8 normal-mode launcher overrides
+// the split at 64 and 256 pairs (one wavefront, below).
 struct RowSplit {
   int nv;     // vectors per lane
   int waves;  // wavefronts per block (row pieces, padded)
