@@ -34,8 +34,9 @@ __device__ __forceinline__ uint64_t first_rows(int myrow, int K) {
 }
 
 // RM (rank-major): sum the token's distinct rows with weight 1 and skip the
-// loads of repeated rows.
-template <int NV, bool RM>
+// loads of repeated rows.  SERIAL (one vector per lane): one row load in
+// flight per wavefront, each waiting for the previous one.
+template <int NV, bool RM, bool SERIAL = false>
 __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y,
                                                      const int32_t* __restrict__ send_pos,
                                                      const float* __restrict__ w,
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
   const float myw = RM ? 1.0f : (lane < K ? w[(int64_t)tok * K + lane] : 0.0f);
   const uint64_t keep = RM ? first_rows(myrow, K) : ~0ull;
-  constexpr int kGroup = NV == 1 ? 8 : (NV == 2 ? 4 : 2);
+  constexpr int kGroup = SERIAL ? 1 : (NV == 1 ? 8 : (NV == 2 ? 4 : 2));
   float acc[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -235,6 +236,20 @@ static void launch_rows(const CombineArgs& a, int nv, int V, int waves, hipStrea
   }
 }
 
+// Kernel choice by measurement on MI355X (prefill routing, 8 x 4096 tokens,
+// top-8; interleaved runs per box):
+//  - normal and low-latency modes at hidden 7168-8192 or up to 2048: one
+//    token per block, one row load in flight per wavefront (combine_rows
+//    SERIAL): at 7168 2.4% faster than the two-token pipeline, at 2048
+//    4.9% (the decode shape, 1,024 tokens: 3%);
+//  - otherwise, from 8,192 tokens with top-k <= 8, the two-token pipeline
+//    (outputs staged in LDS up to hidden 4096) -- best at 4096-6144 --
+//    except rank-major rows wider than 4096, where one token per block with
+//    eight row loads in flight is 4% faster;
+//  - otherwise one token per block, eight row loads in flight.
+constexpr int kSerialMinVectors = 896;  // hidden 7168
+constexpr int kSerialMaxVectors = 256;  // hidden 2048
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int64_t N = (int64_t)a.g.R * a.g.T;
   if (N == 0) return hipSuccess;
@@ -242,19 +257,23 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   int nv = 1;
   while ((V + kWave * nv - 1) / (kWave * nv) > 16) ++nv;
   const int waves = (V + kWave * nv - 1) / (kWave * nv);
+  const u32x4* y = (const u32x4*)a.y;
+  u32x4* out = (u32x4*)a.out;
+  if (nv == 1 && !a.rank_major && (V >= kSerialMinVectors || V <= kSerialMaxVectors)) {
+    hipLaunchKernelGGL((combine_rows<1, false, true>), dim3((unsigned)N), dim3(kWave * waves), 0,
+                       st, y, a.send_pos, a.w, out, V, a.g.K, a.y_rows, a.err);
+    return hipGetLastError();
+  }
   // two tokens per block only when there are enough blocks to fill the chip
-  if (nv == 1 && a.g.K <= kPipeK && N >= kPipeMinTokens) {
+  const bool pipe = nv == 1 && a.g.K <= kPipeK && N >= kPipeMinTokens &&
+                    !(a.rank_major && V > kStageMaxVectors);
+  if (pipe) {
     const int n = (int)N;
     const dim3 grid((n + kPipeTokens - 1) / kPipeTokens), block(kWave * waves);
     const bool stage = V <= kStageMaxVectors;
     const size_t lds = stage ? sizeof(u32x4) * (size_t)kPipeTokens * V : 0;
-    const u32x4* y = (const u32x4*)a.y;
-    u32x4* out = (u32x4*)a.out;
     if (a.rank_major && stage)
       hipLaunchKernelGGL((combine_rows_pipe<true, true>), grid, block, lds, st, y, a.send_pos,
-                         a.w, out, V, a.g.K, n, a.y_rows, a.err);
-    else if (a.rank_major)
-      hipLaunchKernelGGL((combine_rows_pipe<true, false>), grid, block, 0, st, y, a.send_pos,
                          a.w, out, V, a.g.K, n, a.y_rows, a.err);
     else if (stage)
       hipLaunchKernelGGL((combine_rows_pipe<false, true>), grid, block, lds, st, y, a.send_pos,
