@@ -241,7 +241,10 @@ static void launch_rows(const CombineArgs& a, int nv, int V, int waves, hipStrea
 //  - normal and low-latency modes at hidden 7168-8192 or up to 2048: one
 //    token per block, one row load in flight per wavefront (combine_rows
 //    SERIAL): at 7168 2.4% faster than the two-token pipeline, at 2048
-//    4.9% (the decode shape, 1,024 tokens: 3%);
+//    4.9%; with fewer than 8,192 tokens at 7168-8192 the wavefronts take
+//    four vectors per lane (the decode shape, 1,024 tokens: 8% faster than
+//    eight loads in flight; at the prefill shape one vector per lane wins
+//    by 9%);
 //  - otherwise, from 8,192 tokens with top-k <= 8, the two-token pipeline
 //    (outputs staged in LDS up to hidden 4096) -- best at 4096-6144 --
 //    except rank-major rows wider than 4096, where one token per block with
@@ -260,8 +263,15 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const u32x4* y = (const u32x4*)a.y;
   u32x4* out = (u32x4*)a.out;
   if (nv == 1 && !a.rank_major && (V >= kSerialMinVectors || V <= kSerialMaxVectors)) {
-    hipLaunchKernelGGL((combine_rows<1, false, true>), dim3((unsigned)N), dim3(kWave * waves), 0,
-                       st, y, a.send_pos, a.w, out, V, a.g.K, a.y_rows, a.err);
+    if (V >= kSerialMinVectors && N < kPipeMinTokens) {
+      // few tokens (decode): four vectors per lane, 5% faster at 1,024 tokens
+      const int w4 = (V + kWave * 4 - 1) / (kWave * 4);
+      hipLaunchKernelGGL((combine_rows<4, false, true>), dim3((unsigned)N), dim3(kWave * w4), 0,
+                         st, y, a.send_pos, a.w, out, V, a.g.K, a.y_rows, a.err);
+    } else {
+      hipLaunchKernelGGL((combine_rows<1, false, true>), dim3((unsigned)N), dim3(kWave * waves),
+                         0, st, y, a.send_pos, a.w, out, V, a.g.K, a.y_rows, a.err);
+    }
     return hipGetLastError();
   }
   // two tokens per block only when there are enough blocks to fill the chip
