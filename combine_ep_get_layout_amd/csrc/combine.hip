@@ -6,11 +6,12 @@
 // walks dispatch's address book backwards; sec. 5: combine is the inverse
 // of dispatch; sec. 1.1: bf16 combine.
 //
-// Work split: one block per token, one wavefront per piece of the output row
-// (the whole row in flight at once).  The K row indices and weights are
+// Work split: one block per token (two in the pipelined form), one
+// wavefront per piece of the output row.  The K row indices and weights are
 // loaded once per wave (one lane each) and read as scalars; the receive rows
-// stream in with 16-byte non-temporal loads, eight rows' loads issued before
-// their multiply-adds.
+// stream in with 16-byte non-temporal loads.  How many row loads a
+// wavefront keeps in flight (one, or eight before their multiply-adds) is
+// chosen per shape by measurement (launch_combine, below).
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -19,7 +20,8 @@ namespace ep {
 // One block per token, one wavefront per row piece (NV vectors per lane);
 // the K rows are read in groups with all loads of a group issued before its
 // fused multiply-adds (8 rows per group for one vector per lane, fewer for
-// wider pieces so the loads stay in registers).
+// wider pieces so the loads stay in registers; one row per group in the
+// SERIAL form).
 
 // Rank-major mode: a token's entries on one destination rank share a row;
 // bit k is set for the first entry of each distinct row (lanes k < K hold
@@ -34,8 +36,8 @@ __device__ __forceinline__ uint64_t first_rows(int myrow, int K) {
 }
 
 // RM (rank-major): sum the token's distinct rows with weight 1 and skip the
-// loads of repeated rows.  SERIAL (one vector per lane): one row load in
-// flight per wavefront, each waiting for the previous one.
+// loads of repeated rows.  SERIAL: one row's loads (NV vectors per lane) in
+// flight per wavefront, each row waiting for the previous one.
 template <int NV, bool RM, bool SERIAL = false>
 __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y,
                                                      const int32_t* __restrict__ send_pos,
@@ -264,7 +266,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   u32x4* out = (u32x4*)a.out;
   if (nv == 1 && !a.rank_major && (V >= kSerialMinVectors || V <= kSerialMaxVectors)) {
     if (V >= kSerialMinVectors && N < kPipeMinTokens) {
-      // few tokens (decode): four vectors per lane, 5% faster at 1,024 tokens
+      // few tokens (decode): four vectors per lane, 5% faster than one at
+      // 1,024 tokens
       const int w4 = (V + kWave * 4 - 1) / (kWave * 4);
       hipLaunchKernelGGL((combine_rows<4, false, true>), dim3((unsigned)N), dim3(kWave * w4), 0,
                          st, y, a.send_pos, a.w, out, V, a.g.K, a.y_rows, a.err);

@@ -130,14 +130,15 @@ __device__ __forceinline__ int fused_token_rows(const LayoutArgs& a, int64_t tok
   return row;
 }
 
-// The layout's per-expert and per-rank outputs, written by block b for
-// expert b (and rank b), plus the alignment padding rows of expert b's
-// segment.  Every block of a fused dispatch calls this first.
+// The same, loading the token's entries itself.
 __device__ __forceinline__ int fused_token_rows(const LayoutArgs& a, int64_t tok, bool writer,
                                                 const int* start) {
   return fused_token_rows(a, tok, writer, start, fused_token_entries(a, tok));
 }
 
+// The layout's per-expert and per-rank outputs, written by block b for
+// expert b (and rank b), plus the alignment padding rows of expert b's
+// segment.  Every block of a fused dispatch calls this first.
 __device__ __forceinline__ void fused_publish(const LayoutArgs& a, const int* start) {
   const Geometry& g = a.g;
   const int b = blockIdx.x;
@@ -261,16 +262,6 @@ __global__ __launch_bounds__(128) void dispatch_copy_lds(const u32x4* __restrict
 
 // P = 16-channel pairs per row (H / 16); a group of 128 channels is 8
 // pairs = 8 consecutive lanes, reduced with DPP.
-// Work-groups are dealt to the kXcds dies round-robin (block b on die
-// b % kXcds).  xcd_run maps block b to item (b % kXcds) * per + b / kXcds,
-// per = ceil(n / kXcds): each die walks a contiguous run of items in order.
-// A grid of kXcds * per blocks covers every item once (items >= n exit).
-constexpr int kXcds = 8;
-
-__device__ __forceinline__ int xcd_run(int b, int n) {
-  const int per = (n + kXcds - 1) / kXcds;
-  return (b % kXcds) * per + b / kXcds;
-}
 
 template <int NP, int Q, bool LL, bool RM, bool FU>
 __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4* __restrict__ x,
@@ -286,7 +277,7 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
     fused_publish(la, start);
   }
   // blocks past the token grid only publish (fused), never alias a token
-  if ((int)blockIdx.x >= (LL ? kXcds * ((n_tok + kXcds - 1) / kXcds) : n_tok)) return;
+  if ((int)blockIdx.x >= (LL ? xcd_blocks(n_tok) : n_tok)) return;
   // low-latency: die blockIdx.x % kXcds takes a contiguous run of tokens, so
   // consecutive slots of an expert (consecutive tokens) are stored from one
   // L2 and their 4-byte column-major scales merge into whole lines there
@@ -475,7 +466,7 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
   // normal and rank-major modes: rows also index the staging buffer, so they
   // stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
-  const int blocks = LL ? kXcds * ((N + kXcds - 1) / kXcds) : N;
+  const int blocks = LL ? xcd_blocks(N) : N;
   if (a.fused && !RM)
     hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, false, true>), dim3(fused_blocks(a, blocks)),
                        dim3(kWave * waves), 0, st, (const u32x4*)a.x, a.send_pos,

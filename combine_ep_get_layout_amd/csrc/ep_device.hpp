@@ -38,6 +38,22 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int nbits, uint64_t 
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Work-groups are dealt to the kXcds dies round-robin (block b on die
+// b % kXcds), and each die has its own L2.  xcd_run maps block b to item
+// (b % kXcds) * per + b / kXcds, per = ceil(n / kXcds): each die walks a
+// contiguous run of items in order.  A grid of xcd_blocks(n) = kXcds * per
+// blocks covers every item once (items >= n exit).
+constexpr int kXcds = 8;
+
+__host__ __device__ __forceinline__ int xcd_blocks(int n) {
+  return kXcds * ((n + kXcds - 1) / kXcds);
+}
+
+__device__ __forceinline__ int xcd_run(int b, int n) {
+  const int per = (n + kXcds - 1) / kXcds;
+  return (b % kXcds) * per + b / kXcds;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

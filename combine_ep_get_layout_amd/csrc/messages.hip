@@ -16,10 +16,12 @@
 //               over sources; descriptor count of each message).
 //   2. rows   : one block per source: arena bases rounded to the region size,
 //               first descriptor of each message, the table row.
-//   3. pack   : one wavefront per token row piece.  The row is read once and
-//               quantised once, then stored into every message that carries
-//               the token, at index send_head[s][t][d] within the message,
-//               with the token's scales, weights, expert ids and index.
+//   3. pack   : one wavefront per token row piece, four tokens per block,
+//               each die taking a contiguous run of tokens.  The row is read
+//               once and quantised once, then stored into every message that
+//               carries the token, at index send_head[s][t][d] within the
+//               message, with the token's scales, weights, expert ids and
+//               index.
 //   4. finish : one thread per message: section padding, header, then (after
 //               a fence) the completion flag, then the descriptors.
 #include "ep_device.hpp"
@@ -232,7 +234,15 @@ template <int NP, int Q>
 __global__ __launch_bounds__(256) void msg_pack_fp8(MessageArgs a, int P) {
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63;
-  const int tok = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+  // four tokens per block; each die takes a contiguous run of blocks, so
+  // consecutive tokens of a message (adjacent scale, weight and id entries)
+  // are stored from one L2 and their cache lines merge there (measured on
+  // MI355X at the 64-rank message workload: the pack unchanged, the
+  // delivery that reads the messages next 1% faster)
+  const int nblk = (g.R * g.T + 3) / 4;
+  const int blk = xcd_run(blockIdx.x, nblk);
+  if (blk >= nblk) return;
+  const int tok = uniform(blk * 4 + (threadIdx.x >> 6));
   if (tok >= g.R * g.T) return;
   const int piece = blockIdx.y;
   const int base = piece * kWave * NP;
@@ -279,7 +289,11 @@ template <int NV>
 __global__ __launch_bounds__(256) void msg_pack_bf16(MessageArgs a, int V) {
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63;
-  const int tok = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+  // the FP8 packer's die-aware block order
+  const int nblk = (g.R * g.T + 3) / 4;
+  const int blk = xcd_run(blockIdx.x, nblk);
+  if (blk >= nblk) return;
+  const int tok = uniform(blk * 4 + (threadIdx.x >> 6));
   if (tok >= g.R * g.T) return;
   const int piece = blockIdx.y;
   const int base = piece * kWave * NV;
@@ -381,7 +395,8 @@ static void launch_pack_fp8(const MessageArgs& a, hipStream_t st) {
   const int P = a.g.H / 16;
   const int npieces = (P + kWave * NP - 1) / (kWave * NP);
   const int N = a.g.R * a.g.T;
-  hipLaunchKernelGGL((msg_pack_fp8<NP, Q>), dim3((N + 3) / 4, npieces), dim3(256), 0, st, a, P);
+  hipLaunchKernelGGL((msg_pack_fp8<NP, Q>), dim3(xcd_blocks((N + 3) / 4), npieces), dim3(256), 0,
+                     st, a, P);
 }
 
 template <int Q>
@@ -406,7 +421,8 @@ static void launch_pack_bf16(const MessageArgs& a, hipStream_t st) {
   const int V = a.g.H / 8;
   const int npieces = (V + kWave * NV - 1) / (kWave * NV);
   const int N = a.g.R * a.g.T;
-  hipLaunchKernelGGL(msg_pack_bf16<NV>, dim3((N + 3) / 4, npieces), dim3(256), 0, st, a, V);
+  hipLaunchKernelGGL(msg_pack_bf16<NV>, dim3(xcd_blocks((N + 3) / 4), npieces), dim3(256), 0, st,
+                     a, V);
 }
 
 size_t message_ws_bytes(int R) { return sizeof(int64_t) * (4 * (size_t)R * R + 2 * (size_t)R); }

@@ -147,15 +147,14 @@ __global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
   for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
 }
 
-// Unpack: one block per (s, d); wavefront w takes local experts w, w +
-// waves, ...  XCD-aware order: workgroups are dealt to the chip's
+// Unpack: one block per (s, d), ranking and copying as described at the
+// top of this file.  Die-aware order: workgroups are dealt to the chip's
 // kXcds dies round-robin, so block b runs on die b % kXcds.  Destination d
 // is given die d % kXcds, and its messages follow in source order on that
 // die: the slots of an expert from consecutive sources are adjacent, and
 // their column-major scale stores (4 bytes each, one cache line per
 // (expert, group) column run) meet in the same L2 instead of being written
 // back as partial lines from eight L2s.
-constexpr int kXcds = 8;
 
 constexpr int kUnpackSeg = 2048;   // entries ranked per round (LDS slots)
 constexpr int kUnpackMaxL = 2048;  // local experts (E <= 2048)
