@@ -1,0 +1,66 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the algorithmic
+byte counts of the prefill shape, and the staleness check that keeps
+counter traffic from being reported for changed kernel code."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from combine_ep_get_layout_amd import inputs  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_prefill_bytes_match_the_closed_form():
+    # dispatch: x read once, K rows written per token, one 4-byte slot read
+    # per routed pair; combine: K rows read and the output written per
+    # token, a slot and a weight read per routed pair
+    w = inputs.WORKLOADS["normal_prefill"]
+    M = w.R * w.T * w.K
+    assert bench.dispatch_bytes(w, M) == 2 * w.H * (w.N + M) + 4 * M
+    assert bench.combine_bytes(w, M) == 2 * w.H * (M + w.N) + 8 * M
+    assert bench.dispatch_bytes(w, M) == 4_228_907_008
+
+
+def test_code_only_ignores_comments_and_spacing():
+    a = "int f(int x) {  // add one\n  return x + 1; /* done */\n}\n"
+    b = "int f(int x) { return x + 1; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(b.replace("+ 1", "+ 2"))
+
+
+def test_traffic_is_dropped_when_the_kernel_code_changed(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    entry = {"kernel_hash": bench.kernel_hash("combine_rows"), "hbm_bytes_per_launch": 123}
+    (prof / "counters.json").write_text(json.dumps({
+        "wl:combine_rows": entry,
+        "wl:dispatch_copy": {"kernel_hash": "0" * 16, "hbm_bytes_per_launch": 456},
+    }))
+    real_root = bench.ROOT
+    # counters are read from the temporary folder, sources from the repository
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = tmp_path / "combine_ep_get_layout_amd"
+    src.symlink_to(os.path.join(real_root, "combine_ep_get_layout_amd"))
+    assert bench.traffic_from_profile("combine_rows", "wl") == 123
+    assert bench.traffic_from_profile("dispatch_copy", "wl") is None
+    assert bench.traffic_from_profile("combine_rows", "other") is None
+
+
+@pytest.mark.parametrize("kernel", sorted(bench.KERNEL_SOURCES))
+def test_every_profiled_kernel_names_existing_sources(kernel):
+    for f in bench.KERNEL_SOURCES[kernel]:
+        assert os.path.isfile(os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc", f)), f
+    assert len(bench.kernel_hash(kernel)) == 16
