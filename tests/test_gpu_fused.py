@@ -35,7 +35,27 @@ def buffers(p, w, total):
     return lay, recv
 
 
-@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+def draw(i):
+    """A random case: both modes, every payload format, alignment, masked and
+    duplicate ids, and token counts on both sides of the one-launch layout's
+    limit (6,144 entries)."""
+    g = np.random.default_rng(5300 + i)
+    mode = int(g.choice([N, L]))
+    R = int(g.choice([1, 2, 3, 4, 8, 16] if mode == N else [1, 2, 4, 8]))
+    E = R * int(g.integers(1, 17 if mode == N else 9))
+    K = int(g.integers(1, min(E, 10) + 1))
+    T = int(g.choice([1, 40, 300, 1000, 2100] if mode == N else [1, 40, 200, 500]))
+    quant = int(g.choice([0, QF, QU]))
+    H = int(8 * g.integers(1, 120)) if quant == 0 else int(128 * g.integers(1, 6))
+    align = int(g.choice([1, 1, 2, 8])) if mode == N else 1
+    return (f"fuzz{i}", R, T, H, E, K, mode, quant, align, float(g.choice([0.0, 0.1, 0.3])),
+            float(g.choice([0.0, 0.3])) if K > 1 else 0.0)
+
+
+FUZZ = [draw(i) for i in range(20)]
+
+
+@pytest.mark.parametrize("c", CASES + FUZZ, ids=[c[0] for c in CASES + FUZZ])
 def test_fused_equals_separate_calls_and_oracle(c):
     name, R, T, H, E, K, mode, quant, align, mfrac, dfrac = c
     say("fused", c)
