@@ -130,8 +130,18 @@ __global__ __launch_bounds__(256) void msg_offsets(MessageArgs a) {
     const int64_t roff = block_scan64(reg, &tot);
     if (i < R) {
       w.recv_loc[i * R + d] = roff;
-      int64_t soff = 0;  // offset of (i, d) in source i's arena
-      for (int d2 = 0; d2 < d; ++d2) soff += region_of(a.cnt_rank[i * R + d2], g.H, g.K, a.quant);
+      // offset of (i, d) in source i's arena: the regions of i's messages to
+      // destinations before d, their counts loaded sixteen at a time (one
+      // memory latency per sixteen instead of one per destination)
+      int64_t soff = 0;
+      const int32_t* crow = a.cnt_rank + i * R;
+      for (int d0 = 0; d0 < d; d0 += 16) {
+        int n[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) n[q] = d0 + q < d ? crow[d0 + q] : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) soff += region_of(n[q], g.H, g.K, a.quant);
+      }
       w.dcount[i * R + d] = message_descriptors(reg, soff, roff, a.region_bytes);
     }
     if (i == 0) w.recv_tot[d] = tot;
@@ -163,9 +173,19 @@ __global__ __launch_bounds__(256) void msg_rows(MessageArgs a) {
       a.arena_base[j] = base_s[j];
       a.arena_base[R + 1 + j] = base_r[j];
     }
-  // descriptors of sources before s
+  // descriptors of sources before s, eight loads per thread in flight
   int64_t part = 0;
-  for (int64_t j = i; j < (int64_t)s * R; j += blockDim.x) part += w.dcount[j];
+  const int64_t nbefore = (int64_t)s * R;
+  for (int64_t j0 = i; j0 < nbefore; j0 += 8 * (int64_t)blockDim.x) {
+    int64_t c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t j = j0 + q * (int64_t)blockDim.x;
+      c[q] = j < nbefore ? w.dcount[j] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) part += c[q];
+  }
   int64_t before;
   block_scan64(part, &before);
   const int64_t dc = i < R ? w.dcount[s * R + i] : 0;
