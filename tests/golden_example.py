@@ -1,0 +1,64 @@
+"""The hand-worked routing example in tests/golden/layout_worked_example.json
+(its derivation and page citations are in the file): expected layouts for
+the normal (alignment 1 and 4), low-latency and rank-major modes, and exact
+combine results with the identity expert.  Shared by the oracle test and
+the GPU test; holds no method arithmetic beyond building the inputs the
+file describes."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+EX = json.load(open(os.path.join(HERE, "golden", "layout_worked_example.json")))
+R, T, H, E, K = (EX["problem"][k] for k in ("R", "T", "H", "E", "K"))
+TOPK = np.array(EX["topk_idx"], np.int32)
+W = np.array(EX["topk_weights"], np.float32)
+# mode name -> (mode number, expert alignment, fixture section)
+MODES = {"normal_align1": (0, 1), "normal_align4": (0, 4), "low_latency": (1, 1),
+         "rank_major": (3, 1)}
+COMMON = ["num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank",
+          "rank_prefix_matrix", "recv_tokens_per_expert", "send_head"]
+PER_MODE = ["expert_start", "rows_per_rank", "row_base", "send_pos"]
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    b = np.ascontiguousarray(v, np.float32).view(np.uint32)
+    assert not np.any(b & 0xFFFF), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def x_values() -> np.ndarray:
+    tok = np.arange(R * T, dtype=np.float32).reshape(R, T, 1)
+    ch = np.arange(H, dtype=np.float32).reshape(1, 1, H)
+    return (tok + 1) * (ch + 1) / 4
+
+
+def expected_out(section: str) -> np.ndarray:
+    key = "rank_major_combine_scale" if section == "rank_major" else "combine_scale"
+    scale = np.array(EX[key], np.float32).reshape(R, T, 1)
+    return bf16_bits(x_values() * scale)
+
+
+def expected_rows(section: str) -> dict[int, int]:
+    """Receive row -> source token (s*T + t) for every filled row; -1 for
+    alignment padding rows."""
+    sec = EX[section]
+    if "recv_src_idx" in sec:
+        return {r: v for r, v in enumerate(sec["recv_src_idx"])}
+    return {int(r): v for r, v in sec["filled_rows"].items()}
+
+
+def check_layout(get, section: str):
+    """`get(name)` returns the layout array of that name as numpy."""
+    for f in COMMON:
+        assert np.array_equal(get(f), np.array(EX[f])), f
+    sec = EX[section]
+    for f in PER_MODE:
+        assert np.array_equal(get(f), np.array(sec[f])), (section, f)
+    src = get("recv_src_idx")
+    for r, v in expected_rows(section).items():
+        assert int(src[r]) == v, (section, r)
