@@ -447,7 +447,22 @@ def cpu_baseline(w, host, tokens_per_rank, min_seconds):
                       f"+ combine, {passes} passes in {total:.1f} s ({dt:.2f} s per pass), "
                       f"single thread",
             "tokens_per_s": round(w.R * T / dt, 1),
-            "phase_s": {k: round(v / passes, 4) for k, v in ph.items()}}
+            "phase_s": {k: round(v / passes, 4) for k, v in ph.items()},
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host's logical CPU count and model (the oracle uses one of them)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "model": model}
 
 
 def main():

@@ -64,3 +64,9 @@ def test_every_profiled_kernel_names_existing_sources(kernel):
     for f in bench.KERNEL_SOURCES[kernel]:
         assert os.path.isfile(os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc", f)), f
     assert len(bench.kernel_hash(kernel)) == 16
+
+
+def test_host_cpu_reports_count_and_model():
+    h = bench.host_cpu()
+    assert h["nproc"] == os.cpu_count()
+    assert h["model"] is None or isinstance(h["model"], str)
