@@ -214,8 +214,9 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
  * layout's notify step into the dispatch kernel): the outputs of
  * ep_get_layout and of ep_dispatch, with the last step of the layout (each
  * entry's row, send_pos, recv_src_idx, send_head, the segment starts) taken
- * by the dispatch kernel itself, so the call issues three launches instead
- * of four (two for problems small enough for the one-launch layout).
+ * by the dispatch kernel itself, so the call issues one launch fewer than
+ * ep_get_layout followed by ep_dispatch (as many for problems small enough
+ * for the one-launch layout, which it then runs before the dispatch).
  * Arguments as for ep_get_layout and ep_dispatch; normal and low-latency
  * modes (EP_ERR_MODE otherwise).  The workspace is used by both steps. */
 int ep_dispatch_fused(const ep_problem* p, const int32_t* topk_idx, const ep_layout* layout,
