@@ -15,7 +15,7 @@
 // Execute, two launches:
 //   1. every descriptor except the last one of each message (its flag), cut
 //      into pieces of at most kPieceBytes; one block per (descriptor, piece)
-//      copies with 16-byte vectors, four per thread in flight;
+//      copies with 16-byte vectors through LDS, 64 KiB per round;
 //   2. one thread per message copies its flag.
 //   The launch boundary puts every payload and header before every flag.
 // Unpack, one launch: one block of eight wavefronts per (source,
@@ -73,25 +73,29 @@ __device__ inline int read_put(const ExecArgs& a, int64_t i, Put* p) {
   return 0;
 }
 
-// Copies bytes [lo, hi) of a put with the threads of the block.
+// Copies bytes [lo, hi) of a put with the threads of the block; every
+// thread of the block must call it (it synchronises the block).  Aligned
+// puts go through LDS in 64 KiB rounds: the block loads a round (each
+// thread one vector in flight at a time), then stores it.  Measured on
+// MI355X at the 64-rank message workload: 0.7% faster than keeping four
+// vectors per thread in flight in registers; 32 KiB rounds gain 0.2% and
+// 128 KiB rounds (one block per CU) are 11% slower.
+constexpr int kCopyRound = 4096;  // vectors of LDS per block
+
 __device__ inline void copy_range(const ExecArgs& a, const Put& p, int64_t lo, int64_t hi) {
   const uint8_t* src = a.send + p.src;
   uint8_t* dst = a.recv + p.dst;
   if (((p.src | p.dst | lo | hi) & 15) == 0) {
-    // four vectors per thread in flight: loads of a round before its stores
+    __shared__ u32x4 stage[kCopyRound];
     const u32x4* s4 = (const u32x4*)(src + lo);
     u32x4* d4 = (u32x4*)(dst + lo);
-    const int64_t nv = (hi - lo) / 16, step = blockDim.x;
-    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += 4 * step) {
-      u32x4 t[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t v = v0 + q * step;
-        t[q] = s4[v < nv ? v : nv - 1];
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (v0 + q * step < nv) d4[v0 + q * step] = t[q];
+    const int64_t nv = (hi - lo) / 16;
+    for (int64_t c0 = 0; c0 < nv; c0 += kCopyRound) {
+      const int n = (int)min((int64_t)kCopyRound, nv - c0);
+      for (int j = threadIdx.x; j < n; j += blockDim.x) stage[j] = s4[c0 + j];
+      __syncthreads();
+      for (int j = threadIdx.x; j < n; j += blockDim.x) d4[c0 + j] = stage[j];
+      __syncthreads();
     }
   } else {
     for (int64_t o = lo + threadIdx.x; o < hi; o += blockDim.x) dst[o] = src[o];
