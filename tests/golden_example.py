@@ -62,3 +62,18 @@ def check_layout(get, section: str):
     src = get("recv_src_idx")
     for r, v in expected_rows(section).items():
         assert int(src[r]) == v, (section, r)
+
+
+# The hand-quantised FP8 group (tests/golden/e4m3_worked_example.json).
+FP8 = json.load(open(os.path.join(HERE, "golden", "e4m3_worked_example.json")))
+
+
+def fp8_input_and_codes():
+    """x as bf16 bits [1][1][H] and the expected E4M3 codes [H]."""
+    H8 = FP8["problem"]["H"]
+    x = np.zeros(H8, np.float32)
+    codes = np.zeros(H8, np.uint8)
+    for ch in FP8["channels"]:
+        x[ch["c"]] = ch["x"]
+        codes[ch["c"]] = int(ch["code"], 16)
+    return bf16_bits(x).reshape(1, 1, H8), codes

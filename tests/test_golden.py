@@ -37,3 +37,23 @@ def test_fixture_is_self_consistent():
     assert np.array_equal(rpm, np.array(EX["rank_prefix_matrix"]))
     assert EX["normal_align1"]["row_base"][-1] == int(np.sum(TOPK >= 0))
     assert EX["rank_major"]["row_base"][-1] == int(np.sum(EX["is_token_in_rank"]))
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["normal", "low_latency"])
+@pytest.mark.parametrize("quant", [1, 2], ids=["fp32_scale", "ue8m0"])
+def test_oracle_matches_hand_quantised_group(quant, mode):
+    from golden_example import FP8, fp8_input_and_codes
+    x, codes = fp8_input_and_codes()
+    pr = FP8["problem"]
+    p = orc.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=mode, quant=quant)
+    topk = np.zeros((1, 1, 1), np.int32)
+    lay = orc.layout(p, topk)
+    cap = 1
+    assert lay.send_pos.reshape(-1)[0] == 0
+    err, recv, scales = orc.dispatch(p, x, topk, lay.send_pos, cap)
+    assert err == 0
+    assert np.array_equal(recv[0], codes)
+    if quant == 1:
+        assert scales.reshape(-1)[0] == np.float32(FP8["fp32_scale"])
+    else:
+        assert int(scales.reshape(-1)[0]) == FP8["ue8m0_byte"]

@@ -59,3 +59,30 @@ def test_hip_matches_worked_example(section, fused):
     torch.cuda.synchronize()
     assert int(h(lay.err)[0]) == 0
     assert np.array_equal(h(out.view(torch.int16)).view(np.uint16), expected_out(section))
+
+
+@pytest.mark.parametrize("mode", [ep.MODE_NORMAL, ep.MODE_LOW_LATENCY], ids=["normal", "low_latency"])
+@pytest.mark.parametrize("quant", [ep.QUANT_FP8_F32, ep.QUANT_FP8_UE8M0], ids=["fp32_scale", "ue8m0"])
+def test_hip_matches_hand_quantised_group(quant, mode):
+    from golden_example import FP8, fp8_input_and_codes
+    say("golden fp8", quant, mode)
+    x, codes = fp8_input_and_codes()
+    pr = FP8["problem"]
+    p = ep.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=mode, quant=quant)
+    cap = ep.max_recv_rows(p)
+    lay = ep.Layout(p, recv_capacity=cap)
+    ws = ep.workspace(p)
+    tk = torch.zeros((1, 1, 1), dtype=torch.int32, device=DEV)
+    ep.get_layout(p, tk, lay, ws)
+    recv = ep.Recv(p, cap)
+    xg = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    ep.dispatch(p, lay, xg, recv=recv, ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    assert int(h(lay.send_pos).reshape(-1)[0]) == 0
+    assert np.array_equal(h(recv.x)[0], codes)
+    sc = h(recv.scales).reshape(-1)[0]
+    if quant == ep.QUANT_FP8_F32:
+        assert sc == np.float32(FP8["fp32_scale"])
+    else:
+        assert int(sc) == FP8["ue8m0_byte"]
