@@ -77,3 +77,61 @@ def fp8_input_and_codes():
         x[ch["c"]] = ch["x"]
         codes[ch["c"]] = int(ch["code"], 16)
     return bf16_bits(x).reshape(1, 1, H8), codes
+
+
+# The hand-worked messages (tests/golden/message_worked_example.json).
+MSG = json.load(open(os.path.join(HERE, "golden", "message_worked_example.json")))
+
+
+def message_inputs():
+    """x [R][T][H] bf16 bits (each token the hand-quantised group), routing and
+    weights as the file gives them, and the group's expected codes."""
+    x1, codes = fp8_input_and_codes()
+    pr = MSG["problem"]
+    x = np.repeat(x1, pr["R"] * pr["T"], axis=0).reshape(pr["R"], pr["T"], pr["H"])
+    return (x, np.array(MSG["topk_idx"], np.int32), np.array(MSG["topk_weights"], np.float32),
+            codes)
+
+
+def _u32(b, o):
+    return int.from_bytes(bytes(b[o:o + 4]), "little")
+
+
+def _be(b, o, n):
+    return int.from_bytes(bytes(b[o:o + n]), "big")
+
+
+def check_messages(table, arena_base, desc, num_desc, arena, codes):
+    """Table, arena bases, every descriptor field and every message byte the
+    file fixes, against the hand derivation."""
+    assert np.array_equal(np.asarray(table).reshape(-1), np.array(MSG["table"]).reshape(-1))
+    assert np.array_equal(np.asarray(arena_base).reshape(-1),
+                          np.array(MSG["arena_base"]).reshape(-1))
+    assert int(num_desc) == MSG["num_descriptors"]
+    k = MSG["descriptor_constants"]
+    for i, want in enumerate(MSG["descriptors"]):
+        d = np.asarray(desc[i], np.uint8)
+        w0, w1 = _be(d, 0, 4), _be(d, 4, 4)
+        got = {"wqe": w0 >> 8, "qpn": w1 >> 8, "raddr": _be(d, 16, 8), "rkey": _be(d, 24, 4),
+               "len": _be(d, 32, 4), "lkey": _be(d, 36, 4), "laddr": _be(d, 40, 8)}
+        assert got == want, i
+        assert w0 & 0xFF == k["opcode"] and w1 & 0xFF == k["ds"], i
+        assert list(d[8:12]) == [0, 0, 0, k["cq_update"]], i
+        assert not d[12:16].any() and not d[28:32].any() and not d[48:64].any(), i
+    sec = MSG["sections"]
+    for m in MSG["messages"]:
+        b = np.asarray(arena[m["send_offset"]:m["send_offset"] + 224], np.uint8)
+        assert [_u32(b, 4 * j) for j in range(4)] == m["header"]
+        assert [_u32(b, 208 + 4 * j) for j in range(4)] == m["flag"]
+        lo, hi = sec["codes"]
+        assert np.array_equal(b[lo:hi], codes)
+        lo, hi = sec["scales"]
+        assert np.frombuffer(bytes(b[lo:lo + 4]), np.float32)[0] == np.float32(MSG["fp32_scale"])
+        assert not b[lo + 4:hi].any()
+        lo, hi = sec["weights"]
+        assert np.frombuffer(bytes(b[lo:lo + 4]), np.float32)[0] == np.float32(m["weight"])
+        assert not b[lo + 4:hi].any()
+        lo, hi = sec["expert_ids"]
+        assert _u32(b, lo) == m["expert_id"] and not b[lo + 4:hi].any()
+        lo, hi = sec["src_token"]
+        assert _u32(b, lo) == m["src_token"] and not b[lo + 4:hi].any()

@@ -57,3 +57,14 @@ def test_oracle_matches_hand_quantised_group(quant, mode):
         assert scales.reshape(-1)[0] == np.float32(FP8["fp32_scale"])
     else:
         assert int(scales.reshape(-1)[0]) == FP8["ue8m0_byte"]
+
+
+def test_oracle_matches_hand_worked_messages():
+    from golden_example import MSG, check_messages, message_inputs
+    x, topk, wt, codes = message_inputs()
+    pr = MSG["problem"]
+    p = orc.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=2, quant=1,
+                    region_bytes=pr["region_bytes"], epoch=pr["epoch"])
+    om = orc.messages(p, x, topk, wt, 512, 64)
+    assert om.err == 0
+    check_messages(om.table, om.arena_base, om.desc, om.num_desc, om.send_arena, codes)
