@@ -135,3 +135,15 @@ def check_messages(table, arena_base, desc, num_desc, arena, codes):
         assert _u32(b, lo) == m["expert_id"] and not b[lo + 4:hi].any()
         lo, hi = sec["src_token"]
         assert _u32(b, lo) == m["src_token"] and not b[lo + 4:hi].any()
+
+
+def check_unpacked(recv_rows, scales, recv_count, recv_src_idx, codes):
+    """The receiver's low-latency layout against the hand derivation."""
+    u = MSG["unpacked"]
+    assert [int(c) for c in np.asarray(recv_count).reshape(-1)] == u["recv_count"]
+    for r, st in u["rows"].items():
+        r = int(r)
+        assert np.array_equal(np.asarray(recv_rows)[r], codes), r
+        assert int(np.asarray(recv_src_idx).reshape(-1)[r]) == st, r
+        si = u["scale_index"][str(r)]
+        assert np.asarray(scales).reshape(-1)[si] == np.float32(MSG["fp32_scale"]), r

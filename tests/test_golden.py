@@ -60,7 +60,7 @@ def test_oracle_matches_hand_quantised_group(quant, mode):
 
 
 def test_oracle_matches_hand_worked_messages():
-    from golden_example import MSG, check_messages, message_inputs
+    from golden_example import MSG, check_messages, check_unpacked, message_inputs
     x, topk, wt, codes = message_inputs()
     pr = MSG["problem"]
     p = orc.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=2, quant=1,
@@ -68,3 +68,10 @@ def test_oracle_matches_hand_worked_messages():
     om = orc.messages(p, x, topk, wt, 512, 64)
     assert om.err == 0
     check_messages(om.table, om.arena_base, om.desc, om.num_desc, om.send_arena, codes)
+    # delivery and the receiver
+    err, recv = orc.messages_execute(p, om, int(om.arena_base[1][-1]))
+    assert err == 0
+    lay = orc.layout(p, topk)
+    un = orc.messages_unpack(p, recv, om.table, lay.num_tokens_per_expert)
+    assert un.err == 0
+    check_unpacked(un.recv, un.scales, un.recv_count, un.recv_src_idx, codes)

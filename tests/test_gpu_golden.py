@@ -90,9 +90,9 @@ def test_hip_matches_hand_quantised_group(quant, mode):
 
 def test_hip_matches_hand_worked_messages():
     """Packer and descriptors through the C ABI against the hand derivation,
-    then the loopback delivery: each region arrives at its receive offset
-    byte for byte."""
-    from golden_example import MSG, check_messages, message_inputs
+    then the loopback delivery (each region arrives at its receive offset
+    byte for byte) and the receiver's low-latency layout."""
+    from golden_example import MSG, check_messages, check_unpacked, message_inputs
     say("golden messages")
     x, topk, wt, codes = message_inputs()
     pr = MSG["problem"]
@@ -121,3 +121,10 @@ def test_hip_matches_hand_worked_messages():
     for row in np.array(MSG["table"]).reshape(-1, 8):
         if row[2] > 0:
             assert np.array_equal(got[row[1]:row[1] + row[2]], arena[row[0]:row[0] + row[2]])
+    # the receiver
+    recv_cap = int(MSG["arena_base"][1][-1])
+    out, cnt, src = ep.unpack_buffers(p)
+    ep.messages_unpack(p, msgs, recv[:recv_cap], lay.num_tokens_per_expert, out, cnt, src, err)
+    torch.cuda.synchronize()
+    assert int(h(err)[0]) == 0
+    check_unpacked(h(out.x), h(out.scales), h(cnt), h(src), codes)
