@@ -147,3 +147,39 @@ def check_unpacked(recv_rows, scales, recv_count, recv_src_idx, codes):
         assert int(np.asarray(recv_src_idx).reshape(-1)[r]) == st, r
         si = u["scale_index"][str(r)]
         assert np.asarray(scales).reshape(-1)[si] == np.float32(MSG["fp32_scale"]), r
+
+
+# Duplicate expert ids (tests/golden/layout_duplicates.json).
+DUP = json.load(open(os.path.join(HERE, "golden", "layout_duplicates.json")))
+DUP_MODES = {"normal": 0, "low_latency": 1, "rank_major": 3}
+
+
+def dup_inputs():
+    pr = DUP["problem"]
+    R2, T2, H2 = pr["R"], pr["T"], pr["H"]
+    tok = np.arange(R2 * T2, dtype=np.float32).reshape(R2, T2, 1)
+    ch = np.arange(H2, dtype=np.float32).reshape(1, 1, H2)
+    x = (tok + 1) * (ch + 1) / 4
+    return (np.array(DUP["topk_idx"], np.int32), np.array(DUP["topk_weights"], np.float32),
+            bf16_bits(x), x)
+
+
+def check_dup_layout(get, section):
+    for f in COMMON:
+        assert np.array_equal(get(f), np.array(DUP[f])), f
+    sec = DUP[section]
+    assert np.array_equal(get("send_pos"), np.array(sec["send_pos"])), section
+    if "row_base" in sec:
+        assert np.array_equal(get("row_base"), np.array(sec["row_base"])), section
+    src = get("recv_src_idx")
+    rows = ({r: v for r, v in enumerate(sec["recv_src_idx"])} if "recv_src_idx" in sec
+            else {int(r): v for r, v in sec["filled_rows"].items()})
+    for r, v in rows.items():
+        assert int(src[r]) == v, (section, r)
+    return rows
+
+
+def dup_expected_out(section, x):
+    key = "rank_major_combine_scale" if section == "rank_major" else "combine_scale"
+    pr = DUP["problem"]
+    return bf16_bits(x * np.array(DUP[key], np.float32).reshape(pr["R"], pr["T"], 1))

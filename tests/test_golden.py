@@ -75,3 +75,32 @@ def test_oracle_matches_hand_worked_messages():
     un = orc.messages_unpack(p, recv, om.table, lay.num_tokens_per_expert)
     assert un.err == 0
     check_unpacked(un.recv, un.scales, un.recv_count, un.recv_src_idx, codes)
+
+
+@pytest.mark.parametrize("section", ["normal", "low_latency", "rank_major"])
+def test_oracle_matches_duplicate_ids_example(section):
+    from golden_example import DUP, DUP_MODES, check_dup_layout, dup_expected_out, dup_inputs
+    topk, wt, xb, x = dup_inputs()
+    pr = DUP["problem"]
+    p = orc.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=DUP_MODES[section])
+    lay = orc.layout(p, topk)
+    assert lay.err == 0
+    rows = check_dup_layout(lambda f: getattr(lay, f), section)
+    cap = pr["E"] * pr["R"] * pr["T"] if section == "low_latency" else lay.total_rows
+    err, recv, _ = orc.dispatch(p, xb, topk, lay.send_pos, cap)
+    assert err == 0
+    for r, st in rows.items():
+        assert np.array_equal(recv[r], xb.reshape(-1, pr["H"])[st])
+    err, out = orc.combine(p, recv, wt, lay.send_pos)
+    assert err == 0
+    assert np.array_equal(out, dup_expected_out(section, x))
+
+
+def test_oracle_matches_low_latency_overflow_example():
+    from golden_example import DUP
+    o = DUP["overflow"]
+    pr = o["problem"]
+    p = orc.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=1)
+    lay = orc.layout(p, np.array(o["topk_idx"], np.int32))
+    assert lay.err == o["err"]
+    assert np.array_equal(lay.send_pos, np.array(o["send_pos"]))

@@ -128,3 +128,48 @@ def test_hip_matches_hand_worked_messages():
     torch.cuda.synchronize()
     assert int(h(err)[0]) == 0
     check_unpacked(h(out.x), h(out.scales), h(cnt), h(src), codes)
+
+
+@pytest.mark.parametrize("section", ["normal", "low_latency", "rank_major"])
+def test_hip_matches_duplicate_ids_example(section):
+    from golden_example import DUP, DUP_MODES, check_dup_layout, dup_expected_out, dup_inputs
+    say("golden duplicates", section)
+    topk, wt, xb, x = dup_inputs()
+    pr = DUP["problem"]
+    mode = DUP_MODES[section]
+    p = ep.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=mode)
+    cap = ep.max_recv_rows(p)
+    lay = ep.Layout(p, recv_capacity=cap)
+    ws = ep.workspace(p)
+    tk = torch.from_numpy(topk).to(DEV)
+    ep.get_layout(p, tk, lay, ws)
+    recv = ep.Recv(p, cap)
+    xg = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    wtg = torch.from_numpy(wt).to(DEV)
+    kw = dict(topk_idx=tk, topk_weights=wtg) if mode == ep.MODE_RANK_MAJOR else {}
+    ep.dispatch(p, lay, xg, recv=recv, ws=ws, **kw)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    rows = check_dup_layout(lambda f: h(getattr(lay, f)), section)
+    got = h(recv.x.view(torch.int16)).view(np.uint16)
+    for r, st in rows.items():
+        assert np.array_equal(got[r], xb.reshape(-1, pr["H"])[st])
+    out = torch.empty((pr["R"], pr["T"], pr["H"]), dtype=torch.bfloat16, device=DEV)
+    ep.combine(p, lay, recv.x, None if mode == ep.MODE_RANK_MAJOR else wtg, out)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == 0
+    assert np.array_equal(h(out.view(torch.int16)).view(np.uint16), dup_expected_out(section, x))
+
+
+def test_hip_matches_low_latency_overflow_example():
+    from golden_example import DUP
+    o = DUP["overflow"]
+    pr = o["problem"]
+    say("golden overflow")
+    p = ep.Problem(pr["R"], pr["T"], pr["H"], pr["E"], pr["K"], mode=ep.MODE_LOW_LATENCY)
+    lay = ep.Layout(p)
+    ws = ep.workspace(p)
+    ep.get_layout(p, torch.tensor(o["topk_idx"], dtype=torch.int32, device=DEV), lay, ws)
+    torch.cuda.synchronize()
+    assert int(h(lay.err)[0]) == o["err"]
+    assert np.array_equal(h(lay.send_pos), np.array(o["send_pos"]))
