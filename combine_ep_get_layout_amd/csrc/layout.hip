@@ -355,7 +355,7 @@ __device__ void direct_expert_block(const LayoutArgs& a, int e0, int* hist, int*
   int bad = 0;
 #pragma unroll
   for (int q = 0; q < kDirectPer; ++q) {
-    if (lo + q >= hi) break;
+    if (lo + q >= hi) continue;  // lo + q only grows: every later entry is out too
     const int id = ids[q];
 #pragma unroll
     for (int j = 0; j < kDirectExperts; ++j) cnt[j] += id == e0 + j;
