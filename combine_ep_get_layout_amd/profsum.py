@@ -82,6 +82,9 @@ def main():
                   f"Calibration: a plain copy of 2^30 bytes reads FETCH_SIZE = {cal_f[0] / 1e9:.4f} GB "
                   f"and WRITE_SIZE = {cal_w[0] / 1e9:.4f} GB; scale factors {sf:.4f} (fetch), "
                   f"{sw:.4f} (write).", "",
+                  "Values are per launch: the mean over the run's launches of each kernel. "
+                  "bench.py reports the roofline kernel's scaled total as `traffic` "
+                  "(from counters.json, while the kernel's code is unchanged).", "",
                   "| kernel | FETCH raw GB | WRITE raw GB | fetch GB (scaled) | write GB (scaled) | total GB |",
                   "|---|---|---|---|---|---|"]
         for k in sorted(set(f) & set(w), key=lambda k: -(f[k] + w[k])):
