@@ -46,6 +46,11 @@ SMALL = [
     ("ue8ll", 2, 64, 128, 8, 2, 1, LL, QU, 0.0, 0.0, 0),
     ("fp8_htail", 2, 16, 8320, 8, 2, 1, LL, QF, 0.0, 0.0, 0),
     ("empty", 2, 0, 128, 8, 2, 1, N, QN, 0.0, 0.0, 0),
+    # grouped-GEMM tile alignments: chunked and one-launch layouts, the scale
+    # transpose with padding rows
+    ("align128", 4, 600, 256, 32, 4, 128, N, QN, 0.05, 0.0, 0),
+    ("align128_ue8", 4, 300, 512, 16, 8, 128, N, QU, 0.05, 0.05, 0),
+    ("align64_direct", 2, 50, 128, 8, 4, 64, N, QF, 0.1, 0.0, 0),
     # the documented limits: 256 ranks, 2048 experts, top-64, hidden 32768
     ("max_r", 256, 3, 128, 256, 8, 1, N, QN, 0.1, 0.1, 0),
     ("max_r_chunked", 256, 5, 128, 512, 8, 2, N, QN, 0.05, 0.0, 0),
