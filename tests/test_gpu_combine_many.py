@@ -1,13 +1,17 @@
-"""GPU parity of the many-token combine (8192 tokens or more, top-k <= 8,
-hidden <= 8192: several tokens per block with the row loads of the next
-token in flight) through the C ABI, against the oracle on every token.
-
-Small hidden sizes keep the oracle fast while the token count selects the
-many-token kernel; token counts leave a ragged last block.  Covers masked
-entries, k = 1..8, rank-major repeats (a token's entries on one rank share
-a row, summed once), a receive buffer with no rows (every entry masked),
-and a receive buffer shorter than the rows the layout assigns (those
-entries are dropped and the capacity error bit is raised)."""
+"""GPU parity of the combine at 8192 tokens or more through the C ABI,
+against the oracle on every token.  The token count and the hidden size
+select the kernel form:
+ - hidden up to 2048 and 7168-8192: one token per block, one row load in
+   flight per wavefront;
+ - hidden 2056-4096 (outputs staged in LDS) and 4104-7160: two tokens per
+   block with the next token's row loads in flight;
+ - rank-major rows wider than 4096: one token per block, eight row loads in
+   flight.
+Token counts leave a ragged last block.  Covers masked entries, k = 1..8,
+rank-major repeats (a token's entries on one rank share a row, summed
+once), a receive buffer with no rows (every entry masked), and a receive
+buffer shorter than the rows the layout assigns (those entries are dropped
+and the capacity error bit is raised)."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +33,10 @@ CASES = [
     ("rm_k8_dups", 4, 2049, 256, 16, 8, RM, 0.1, 0.3),
     ("rm_k5", 3, 2731, 128, 12, 5, RM, 0.2, 0.0),
     ("all_masked", 2, 4097, 128, 8, 4, N_, 1.0, 0.0),
+    ("h3072_pipe_staged", 2, 4100, 3072, 8, 4, N_, 0.05, 0.1),
+    ("h5120_pipe", 2, 4100, 5120, 8, 4, N_, 0.05, 0.0),
+    ("h8192_serial", 1, 8193, 8192, 4, 3, N_, 0.1, 0.0),
+    ("rm_h5120_eight", 2, 4100, 5120, 8, 4, RM, 0.05, 0.2),
 ]
 
 
@@ -79,7 +87,12 @@ def test_many_token_combine(c):
         assert total == 0
 
 
-@pytest.mark.parametrize("c", [CASES[0], CASES[4]], ids=["normal", "rank_major"])
+SHORT = {c[0]: c for c in CASES}
+
+
+@pytest.mark.parametrize("c", [SHORT["k8_masked"], SHORT["rm_k8_dups"],
+                               SHORT["h3072_pipe_staged"]],
+                         ids=["normal", "rank_major", "pipelined"])
 def test_many_token_combine_short_buffer(c):
     """The last 37 rows are missing from y: their entries are skipped and
     the capacity error bit is set."""
