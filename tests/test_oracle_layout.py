@@ -152,3 +152,43 @@ def test_normal_alignment_segments():
     filled[lay.send_pos.reshape(-1)] = True
     assert (lay.recv_src_idx[~filled] == -1).all()
     assert (lay.recv_src_idx[filled] >= 0).all()
+
+
+try:
+    from hypothesis import HealthCheck, given, settings
+    from hypothesis import strategies as st
+except ImportError:  # pragma: no cover - hypothesis is optional
+    given = None
+
+
+if given is not None:
+    @st.composite
+    def tiny_routings(draw):
+        """Tiny problems with arbitrary ids in [-1, E): masked entries,
+        duplicates within a token, every alignment and both slot modes."""
+        R = draw(st.integers(1, 4))
+        E = R * draw(st.integers(1, 4))
+        K = draw(st.integers(1, min(E, 5)))
+        T = draw(st.integers(0, 10))
+        mode = draw(st.sampled_from([orc.MODE_NORMAL, orc.MODE_LL]))
+        align = draw(st.sampled_from([1, 2, 3, 5])) if mode == orc.MODE_NORMAL else 1
+        ids = draw(st.lists(st.integers(-1, E - 1), min_size=R * T * K, max_size=R * T * K))
+        return R, T, E, K, align, mode, np.array(ids, np.int32).reshape(R, T, K)
+
+    @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+    @given(tiny_routings())
+    def test_layout_matches_brute_force_on_arbitrary_routings(case):
+        R, T, E, K, align, mode, topk = case
+        p = orc.Problem(R, T, 128, E, K, align=align, mode=mode)
+        lay = orc.layout(p, topk)
+        cnt_e, cnt_r, in_rank, rpm, n, start, send_pos, send_head = brute_layout(p, topk)
+        assert np.array_equal(lay.num_tokens_per_expert, cnt_e)
+        assert np.array_equal(lay.num_tokens_per_rank, cnt_r)
+        assert np.array_equal(lay.is_token_in_rank, in_rank)
+        assert np.array_equal(lay.rank_prefix_matrix, rpm)
+        assert np.array_equal(lay.recv_tokens_per_expert, n)
+        assert np.array_equal(lay.expert_start, start)
+        assert np.array_equal(lay.send_pos, send_pos)
+        assert np.array_equal(lay.send_head, send_head)
+        overflow = mode == orc.MODE_LL and (n > R * T).any()
+        assert bool(lay.err & orc.ERR_LL_OVERFLOW) == bool(overflow)
