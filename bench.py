@@ -51,9 +51,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 DEFAULT_WORKLOADS = ["normal_prefill", "ll_decode", "fp8_train", "messages", "rank_prefill"]
-# workloads timed with the fused layout + dispatch call (measured on MI355X:
-# low-latency decode 55.8 -> 53.0 us, FP8 training 2.867 -> 2.829 ms per step;
-# the prefill step is 0.4% slower fused and keeps the two calls)
+# workloads timed with the fused layout + dispatch call (measured on MI355X
+# when it was introduced: low-latency decode 55.8 -> 53.0 us, FP8 training
+# 2.867 -> 2.829 ms per step; the prefill step is 0.5% slower fused, 1.502
+# against 1.494 ms, and keeps the two calls)
 FUSED_WORKLOADS = {"ll_decode", "fp8_train"}
 
 
