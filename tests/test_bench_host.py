@@ -70,3 +70,21 @@ def test_host_cpu_reports_count_and_model():
     h = bench.host_cpu()
     assert h["nproc"] == os.cpu_count()
     assert h["model"] is None or isinstance(h["model"], str)
+
+
+def test_fp8_and_low_latency_bytes_match_the_closed_forms():
+    # low-latency decode: x read once, per routed pair H code bytes + 4G
+    # scale bytes written and a 4-byte slot read; combine as for bf16
+    w = inputs.WORKLOADS["ll_decode"]
+    M, N, H, G = w.R * w.T * w.K, w.N, w.H, w.G
+    assert bench.dispatch_bytes(w, M) == 2 * H * N + (H + 4 * G) * M + 4 * M
+    assert bench.combine_bytes(w, M) == 2 * H * M + 2 * H * N + 8 * M
+    # about 75 MB dispatch (x 14.7 + codes 58.7 + scales 1.8) and 132 MB combine
+    assert round(bench.dispatch_bytes(w, M) / 1e6, 1) == 75.3
+    assert round(bench.combine_bytes(w, M) / 1e6, 1) == 132.2
+    # FP8 training shape: UE8M0 scales are one byte per group
+    w = inputs.WORKLOADS["fp8_train"]
+    M, N, H, G = w.R * w.T * w.K, w.N, w.H, w.G
+    assert bench.dispatch_bytes(w, M) == 2 * H * N + (H + G) * M + 4 * M
+    assert round(bench.dispatch_bytes(w, M) / 1e9, 2) == 5.41
+    assert round(bench.combine_bytes(w, M) / 1e9, 2) == 9.67
