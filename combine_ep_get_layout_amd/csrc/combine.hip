@@ -67,16 +67,13 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
         if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
         row = -1;
       }
-      const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;  // row 0 stands in, weight 0
+      // masked entries, rank-major repeats and rows past y are not read
+      // (row is uniform across the wavefront: no divergence)
+      const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (RM && row < 0) {  // rank-major: a repeated row is not read at all
-          v[kk][i] = u32x4{0u, 0u, 0u, 0u};
-          continue;
-        }
-        v[kk][i] = y_rows > 0 ? __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1))
-                              : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int i = 0; i < NV; ++i)
+        v[kk][i] = row >= 0 ? __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1))
+                            : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int kk = 0; kk < kGroup; ++kk) {
@@ -117,27 +114,18 @@ constexpr int kPipeTokens = 2;
 constexpr int64_t kPipeMinTokens = 8192;
 
 // Loads of one token's (up to kPipeK) rows, one vector per lane.  Rows the
-// mask drops (masked entries, rank-major repeats) are not read in rank-major
-// mode; otherwise row 0 stands in, with weight 0.
+// mask drops (masked entries, rank-major repeats, rows past y) are not read.
 template <bool RM>
 __device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, uint64_t keep,
                                            int K, int j, int V, int64_t y_rows,
                                            u32x4 (&v)[kPipeK]) {
-  if (y_rows == 0) {  // nothing to read; every entry is skipped
-#pragma unroll
-    for (int k = 0; k < kPipeK; ++k) v[k] = u32x4{0u, 0u, 0u, 0u};
-    return;
-  }
 #pragma unroll
   for (int k = 0; k < kPipeK; ++k) {
     int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
     if (RM && !((keep >> k) & 1)) row = -1;
     if (row >= y_rows) row = -1;
-    if (RM && row < 0) {
-      v[k] = u32x4{0u, 0u, 0u, 0u};
-      continue;
-    }
-    v[k] = __builtin_nontemporal_load(y + (int64_t)(row < 0 ? 0 : row) * V + min(j, V - 1));
+    v[k] = row >= 0 ? __builtin_nontemporal_load(y + (int64_t)row * V + min(j, V - 1))
+                    : u32x4{0u, 0u, 0u, 0u};
   }
 }
 

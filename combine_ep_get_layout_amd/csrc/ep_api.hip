@@ -6,6 +6,7 @@
 
 #include "../../include/ep.h"
 #include "ep_internal.hpp"
+#include "msg_format.hpp"
 
 namespace ep {
 size_t message_ws_bytes(int R);
@@ -58,7 +59,9 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
     if (entries + (int64_t)E * (p->expert_alignment - 1) >= (1ll << 31)) return EP_ERR_SHAPE;
   }
   if (p->mode == EP_MODE_MESSAGES) {
-    if (p->region_bytes < 16 || p->region_bytes % 16 != 0) return EP_ERR_SHAPE;
+    // a piece's length is a 32-bit descriptor field and never exceeds a region
+    if (p->region_bytes < 16 || p->region_bytes % 16 != 0 || p->region_bytes > 0xFFFFFFF0ll)
+      return EP_ERR_SHAPE;
   }
   g->R = R;
   g->T = T;
@@ -123,6 +126,90 @@ int64_t ep_max_recv_rows(const ep_problem* p) {
   if (p->mode == EP_MODE_LOW_LATENCY) return (int64_t)g.E * g.R * g.T;
   if (p->mode == EP_MODE_RANK_MAJOR) return (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R);
   return (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Pieces a put of len bytes from arena offset la to arena offset ra is cut
+// into when no piece may cross a multiple of rb on either side: one more
+// than the cut points, which are the multiples of rb strictly inside
+// (la, la + len) on the local side and inside (ra, ra + len) on the remote
+// side.  Both sets have period rb, so they coincide when la = ra (mod rb)
+// and are disjoint otherwise.
+int64_t put_pieces(int64_t la, int64_t ra, int64_t len, int64_t rb) {
+  if (len <= 0) return 0;
+  const int64_t cl = (la + len - 1) / rb - la / rb;
+  const int64_t cr = (ra + len - 1) / rb - ra / rb;
+  return 1 + cl + (la % rb == ra % rb ? 0 : cr);
+}
+
+int64_t region_bytes_of(int64_t n, const ep_problem* p) {
+  return n > 0 ? 32 + ep::msg_sections(n, p->hidden, p->num_topk, p->quant).body : 0;
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+extern "C" {
+
+int ep_messages_capacity(const ep_problem* p, const int32_t* counts, int64_t* send_bytes,
+                         int64_t* recv_bytes, int64_t* descriptors) {
+  Geometry g;
+  const int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (p->mode != EP_MODE_MESSAGES) return EP_ERR_MODE;
+  const int R = g.R;
+  const int64_t rb = p->region_bytes;
+  int64_t send = 0, recv = 0, desc = 0;
+  if (!counts) {
+    // every pair carries T tokens: the largest region, arena and body; a
+    // message's header and flag are one piece each (16 bytes at 16-byte
+    // aligned offsets, rb a multiple of 16), its payload at most one more
+    // than the region boundaries inside it on either side
+    const int64_t reg = region_bytes_of(g.T, p);
+    const int64_t arena = round_up((int64_t)R * reg, rb);
+    send = recv = (int64_t)R * arena;
+    if (reg > 0) desc = (int64_t)R * R * (3 + 2 * ((reg - 32 + rb - 1) / rb));
+  } else {
+    for (int64_t i = 0; i < (int64_t)R * R; ++i)
+      if (counts[i] < 0 || counts[i] > g.T) return EP_ERR_SHAPE;
+    // the packer's own arithmetic: region sizes, offsets inside each rank's
+    // arena (prefix over destinations for a source, over sources for a
+    // destination), arenas rounded up to the region size, then the pieces
+    // of each message's payload, header and flag puts
+    for (int s = 0; s < R; ++s) {
+      int64_t tot = 0;
+      for (int d = 0; d < R; ++d) tot += region_bytes_of(counts[s * R + d], p);
+      send += round_up(tot, rb);
+    }
+    for (int d = 0; d < R; ++d) {
+      int64_t tot = 0;
+      for (int s = 0; s < R; ++s) tot += region_bytes_of(counts[s * R + d], p);
+      recv += round_up(tot, rb);
+    }
+    int64_t recv_loc[256];  // running offset inside each destination's arena (R <= 256)
+    for (int d = 0; d < R; ++d) recv_loc[d] = 0;
+    for (int s = 0; s < R; ++s) {
+      int64_t send_loc = 0;
+      for (int d = 0; d < R; ++d) {
+        const int64_t reg = region_bytes_of(counts[s * R + d], p);
+        if (reg > 0) {
+          const int64_t la = send_loc, ra = recv_loc[d], body = reg - 32;
+          desc += put_pieces(la + 16, ra + 16, body, rb) + put_pieces(la, ra, 16, rb) +
+                  put_pieces(la + 16 + body, ra + 16 + body, 16, rb);
+        }
+        send_loc += reg;
+        recv_loc[d] += reg;
+      }
+    }
+  }
+  if (send_bytes) *send_bytes = send;
+  if (recv_bytes) *recv_bytes = recv;
+  if (descriptors) *descriptors = desc;
+  return EP_OK;
 }
 
 const char* ep_status_string(int s) {

@@ -38,6 +38,17 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int nbits, uint64_t 
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Hand-off point for LDS data one lane of a wavefront stores and other
+// lanes of the same wavefront load afterwards.  The LDS unit executes one
+// wavefront's operations in issue order, so the only hazard is the compiler
+// moving an access across the hand-off; the wavefront-scope fences (no
+// instructions) and the wave barrier forbid that.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Work-groups are dealt to the kXcds dies round-robin (block b on die
 // b % kXcds), and each die has its own L2.  xcd_run maps block b to item
 // (b % kXcds) * per + b / kXcds, per = ceil(n / kXcds): each die walks a

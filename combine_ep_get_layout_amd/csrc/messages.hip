@@ -395,9 +395,14 @@ __global__ __launch_bounds__(256) void msg_finish(MessageArgs a) {
       if (l < c) c = l;
       if (r < c) c = r;
       if (di < a.desc_cap) {
+        // a key holds the region index in 16 bits: a piece past region
+        // 65535 of either arena gets keys naming no rank (the executor
+        // rejects it) and raises the capacity bit
+        const bool fits = la / rb <= kMaxRegionIndex && ra / rb <= kMaxRegionIndex;
+        if (!fits) set_err(a.err, EP_DEVERR_CAPACITY);
         write_desc(a.desc + di * 64, wqe, (uint32_t)(s * R + d), (uint64_t)ra,
-                   (uint32_t)((d << 16) | (ra / rb)), (uint32_t)c, (uint32_t)((s << 16) | (la / rb)),
-                   (uint64_t)la);
+                   fits ? (uint32_t)((d << 16) | (ra / rb)) : kBadKey, (uint32_t)c,
+                   fits ? (uint32_t)((s << 16) | (la / rb)) : kBadKey, (uint64_t)la);
       } else {
         set_err(a.err, EP_DEVERR_CAPACITY);
       }

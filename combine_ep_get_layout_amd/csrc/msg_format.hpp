@@ -37,4 +37,9 @@ __host__ __device__ inline MsgSections msg_sections(int64_t n, int H, int K, int
 
 __device__ __forceinline__ uint32_t be32(uint32_t v) { return __builtin_bswap32(v); }
 
+// Keys: rank << 16 | region index.  Region indices above kMaxRegionIndex do
+// not fit; such a piece gets kBadKey (rank 0xFFFF, never a valid rank).
+constexpr int64_t kMaxRegionIndex = 0xFFFF;
+constexpr uint32_t kBadKey = 0xFFFFFFFFu;
+
 }  // namespace ep

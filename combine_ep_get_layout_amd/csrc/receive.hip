@@ -107,23 +107,27 @@ __device__ inline int64_t live_descriptors(const ExecArgs& a) {
   return n < a.desc_cap ? n : a.desc_cap;
 }
 
-// Launch 1: blockIdx.x = descriptor, blockIdx.y = piece.  Flags are left to
-// launch 2.
+// Launch 1: blockIdx.y = piece; block x takes descriptors x, x + gridDim.x,
+// ... (the grid is at most kExecMaxBlocks wide, whatever the descriptor
+// capacity).  Flags are left to launch 2.
+constexpr int64_t kExecMaxBlocks = 65536;
+
 __global__ __launch_bounds__(kExecThreads) void msg_exec_puts(ExecArgs a, int64_t piece) {
-  const int64_t i = blockIdx.x;
-  if (i >= live_descriptors(a)) return;
-  Put p;
-  const int bad = read_put(a, i, &p);
-  if (bad) {
-    if (blockIdx.y == 0 && threadIdx.x == 0) set_err(a.err, bad);
-    return;
+  const int64_t live = live_descriptors(a);
+  for (int64_t i = blockIdx.x; i < live; i += gridDim.x) {
+    Put p;
+    const int bad = read_put(a, i, &p);  // uniform across the block
+    if (bad) {
+      if (blockIdx.y == 0 && threadIdx.x == 0) set_err(a.err, bad);
+      continue;
+    }
+    const int64_t* row = a.table + ((int64_t)p.s * a.g.R + p.d) * 8;
+    if (i == row[5] + row[6] - 1) continue;  // the message's flag
+    const int64_t lo = (int64_t)blockIdx.y * piece;
+    if (lo >= p.len) continue;
+    const int64_t hi = lo + piece < p.len ? lo + piece : p.len;
+    copy_range(a, p, lo, hi);
   }
-  const int64_t* row = a.table + ((int64_t)p.s * a.g.R + p.d) * 8;
-  if (i == row[5] + row[6] - 1) return;  // the message's flag
-  const int64_t lo = (int64_t)blockIdx.y * piece;
-  if (lo >= p.len) return;
-  const int64_t hi = lo + piece < p.len ? lo + piece : p.len;
-  copy_range(a, p, lo, hi);
 }
 
 // Launch 2: one thread per (s, d) message copies the last descriptor of the
@@ -335,9 +339,11 @@ hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
   const int64_t min_piece = pad16((a.region_bytes + kMaxPieces - 1) / kMaxPieces);
   if (piece < min_piece) piece = min_piece;
   const int64_t pieces = (a.region_bytes + piece - 1) / piece;
-  if (a.desc_cap > 0)
-    hipLaunchKernelGGL(msg_exec_puts, dim3((unsigned)a.desc_cap, (unsigned)pieces),
+  if (a.desc_cap > 0) {
+    const int64_t blocks = a.desc_cap < kExecMaxBlocks ? a.desc_cap : kExecMaxBlocks;
+    hipLaunchKernelGGL(msg_exec_puts, dim3((unsigned)blocks, (unsigned)pieces),
                        dim3(kExecThreads), 0, st, a, piece);
+  }
   const int64_t rr = (int64_t)R * R;
   hipLaunchKernelGGL(msg_exec_flags, dim3((unsigned)((rr + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();

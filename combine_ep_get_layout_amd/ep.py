@@ -21,9 +21,9 @@ MODE_NORMAL, MODE_LOW_LATENCY, MODE_MESSAGES, MODE_RANK_MAJOR = 0, 1, 2, 3
 QUANT_NONE, QUANT_FP8_F32, QUANT_FP8_UE8M0 = 0, 1, 2
 DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY, DEVERR_MESSAGE = 1, 2, 4, 8
 
-EXPORTS = ["ep_workspace_bytes", "ep_max_recv_rows", "ep_get_layout", "ep_dispatch",
-           "ep_dispatch_fused", "ep_combine", "ep_messages_execute", "ep_messages_unpack",
-           "ep_status_string"]
+EXPORTS = ["ep_workspace_bytes", "ep_max_recv_rows", "ep_messages_capacity", "ep_get_layout",
+           "ep_dispatch", "ep_dispatch_fused", "ep_combine", "ep_messages_execute",
+           "ep_messages_unpack", "ep_status_string"]
 
 
 class EPError(RuntimeError):
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         l.ep_workspace_bytes.restype = ctypes.c_size_t
         l.ep_max_recv_rows.argtypes = [P]
         l.ep_max_recv_rows.restype = ctypes.c_int64
+        I64P = ctypes.POINTER(ctypes.c_int64)
+        l.ep_messages_capacity.argtypes = [P, _vp, I64P, I64P, I64P]
+        l.ep_messages_capacity.restype = ctypes.c_int
         l.ep_get_layout.argtypes = [P, _vp, ctypes.POINTER(CLayout), _vp, ctypes.c_size_t, _vp]
         l.ep_get_layout.restype = ctypes.c_int
         l.ep_dispatch.argtypes = [P, ctypes.POINTER(CLayout), _vp, _vp, _vp,
@@ -409,27 +412,26 @@ def messages_unpack(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
                                     _ptr(err), _stream(stream)), "ep_messages_unpack")
 
 
-def messages_capacity(p: Problem, counts=None) -> tuple[int, int]:
-    """(send bytes, descriptors) that suffice.  With per-(s,d) token counts
-    (host [R][R]) the bound is tight to within the arena alignment; without,
-    it is the worst case (every token to every rank)."""
+def messages_sizes(p: Problem, counts=None) -> tuple[int, int, int]:
+    """ep_messages_capacity: (send arena bytes, receive arena bytes,
+    descriptors).  `counts`: host [R][R] tokens per (source, destination)
+    for exact sizes, or None for bounds that hold for every routing."""
     import numpy as np
 
-    R, T, H, K, G = p.R, p.T, p.H, p.K, p.G
-    cb = 2 if p.quant == QUANT_NONE else 1
-    sb = {QUANT_NONE: 0, QUANT_FP8_F32: 4, QUANT_FP8_UE8M0: 1}[p.quant]
+    c = None
+    if counts is not None:
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        _need(c.size == p.R * p.R, "counts [R][R]")
+    out = [ctypes.c_int64(0) for _ in range(3)]
+    _check(lib().ep_messages_capacity(ctypes.byref(p.c()),
+                                      c.ctypes.data if c is not None else None,
+                                      *[ctypes.byref(v) for v in out]), "ep_messages_capacity")
+    return out[0].value, out[1].value, out[2].value
 
-    def pad(v):
-        return (v + 15) // 16 * 16
 
-    def region(n):
-        return 0 if n == 0 else 32 + pad(n * H * cb) + pad(n * G * sb) + 2 * pad(n * K * 4) + pad(n * 4)
-
-    rb = p.region_bytes
-    if counts is None:
-        counts = np.full((R, R), T, np.int64)
-    sizes = np.vectorize(region)(np.asarray(counts, np.int64))
-    send = int(sum((s + rb - 1) // rb * rb for s in sizes.sum(axis=1)))
-    # chunks per put <= 1 + crossings on either side
-    desc = int(sum(3 + 2 * ((r // rb) + 2) for r in sizes.reshape(-1) if r > 0))
+def messages_capacity(p: Problem, counts=None) -> tuple[int, int]:
+    """(send arena bytes, descriptors) for Messages(), from
+    ep_messages_capacity (at least 16 bytes and one descriptor, so the
+    buffers are never empty)."""
+    send, _, desc = messages_sizes(p, counts)
     return max(send, 16), max(desc, 1)

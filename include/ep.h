@@ -165,6 +165,26 @@ size_t ep_workspace_bytes(const ep_problem* p);
  * R*T*min(K, R) for rank-major (every token on K distinct ranks). */
 int64_t ep_max_recv_rows(const ep_problem* p);
 
+/* Buffer sizes of message mode ("Eaas_server" notes: one region per loaded
+ * (source, destination) pair -- header, 16-byte padded body, flag -- packed
+ * into per-rank arenas that start on region boundaries; "ibgda_device.cuh"
+ * notes, sec. 1: every put is cut where it would cross a region boundary of
+ * either arena, one descriptor per piece).  Host only: launches nothing and
+ * reads no device memory.
+ *   counts: host [R][R] int32, tokens of source s sent to rank d (the
+ *           num_tokens_per_rank of ep_get_layout, read back), or NULL for
+ *           bounds that hold for every routing (every token sent to every
+ *           rank: the host-sizing alternative to the read-back, "DeepEP"
+ *           sec. 2.1).
+ *   *send_bytes:  bytes of all send arenas together (arena_base[0][R]);
+ *   *recv_bytes:  bytes of all receive arenas together (arena_base[1][R]);
+ *   *descriptors: descriptors ep_dispatch writes (*num_descriptors).
+ * Exact with counts, upper bounds without.  Output pointers may be NULL.
+ * Returns EP_ERR_MODE unless p->mode is EP_MODE_MESSAGES, EP_ERR_SHAPE for
+ * an invalid problem or a count outside [0, T]; outputs are then untouched. */
+int ep_messages_capacity(const ep_problem* p, const int32_t* counts, int64_t* send_bytes,
+                         int64_t* recv_bytes, int64_t* descriptors);
+
 /* Routing layout ("DeepEP" sec. 2.1, 2.3, 3.2, 4.3): histograms per rank
  * and per expert, is_token_in_rank, the rank prefix matrix, per-expert
  * receive counts and segment starts, and the slot of every routed entry

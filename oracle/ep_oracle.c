@@ -694,9 +694,18 @@ int orc_messages(const orc_problem* p, const uint16_t* x, const int32_t* topk,
           if (RB - la % RB < c) c = RB - la % RB;
           if (RB - ra % RB < c) c = RB - ra % RB;
           if (desc_count < desc_cap) {
-            write_desc(desc + desc_count * 64, wqe, (uint32_t)(s * R + d), (uint64_t)ra,
-                       (uint32_t)((d << 16) | (ra / RB)), (uint32_t)c,
-                       (uint32_t)((s << 16) | (la / RB)), (uint64_t)la);
+            /* a key keeps the region index in its low 16 bits; a piece in
+             * region 65536 or later of either arena cannot be named, so its
+             * keys are all ones (rank 0xFFFF: no such rank) and the capacity
+             * bit is raised */
+            uint32_t rkey = (uint32_t)((d << 16) | (ra / RB));
+            uint32_t lkey = (uint32_t)((s << 16) | (la / RB));
+            if (la / RB > 0xFFFF || ra / RB > 0xFFFF) {
+              rkey = lkey = 0xFFFFFFFFu;
+              err |= ORC_ERR_CAPACITY;
+            }
+            write_desc(desc + desc_count * 64, wqe, (uint32_t)(s * R + d), (uint64_t)ra, rkey,
+                       (uint32_t)c, lkey, (uint64_t)la);
           } else {
             err |= ORC_ERR_CAPACITY;
           }

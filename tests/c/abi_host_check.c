@@ -56,6 +56,40 @@ int main(void) {
   expect(ep_get_layout(NULL, NULL, NULL, NULL, 0, NULL) == EP_ERR_NULL, "layout without problem");
   expect(ep_combine(&p, NULL, NULL, 0, NULL, NULL, NULL) != EP_OK, "combine without arguments");
 
+  /* message sizing, host only.  The 64-rank message shape: a region of n
+   * tokens is 32 bytes (header, flag) plus a body of n*7168 codes, n*56*4
+   * scale bytes, 2 * n*8*4 bytes of weights and ids, n*4 token bytes (all
+   * multiples of 16 at n = 256).  Worst case: every pair carries T = 256
+   * tokens: a region of 1,909,792 bytes; a rank's 64 regions rounded up
+   * to 2 MiB are 59 regions; a body spans at most one 2 MiB boundary, so a
+   * message has at most 1 + 2*1 payload pieces, a header and a flag. */
+  {
+    ep_problem m = p;
+    int64_t sb = -1, rb = -1, nd = -1;
+    m.num_ranks = 64;
+    m.num_tokens = 256;
+    m.mode = EP_MODE_MESSAGES;
+    m.quant = EP_QUANT_FP8_F32;
+    expect(ep_messages_capacity(&m, NULL, &sb, &rb, &nd) == EP_OK, "message sizing ok");
+    expect(sb == (int64_t)64 * 59 * (2 << 20) && rb == sb, "worst-case arena bytes");
+    expect(nd == (int64_t)64 * 64 * 5, "worst-case descriptors");
+    static int32_t counts[64 * 64];
+    memset(counts, 0, sizeof counts);
+    expect(ep_messages_capacity(&m, counts, &sb, &rb, &nd) == EP_OK && sb == 0 && rb == 0 &&
+               nd == 0,
+           "no messages, no bytes");
+    /* one message of one token: region 32 + 7168 + 224 + 32 + 32 + 16 bytes,
+     * rounded up to one 2 MiB region on each side; three pieces */
+    counts[3 * 64 + 5] = 1;
+    expect(ep_messages_capacity(&m, counts, &sb, &rb, &nd) == EP_OK && sb == (2 << 20) &&
+               rb == (2 << 20) && nd == 3,
+           "one message");
+    counts[3 * 64 + 5] = 257; /* more than T tokens */
+    expect(ep_messages_capacity(&m, counts, &sb, &rb, &nd) == EP_ERR_SHAPE, "count above T");
+    m.mode = EP_MODE_NORMAL;
+    expect(ep_messages_capacity(&m, NULL, &sb, &rb, &nd) == EP_ERR_MODE, "sizing outside messages");
+  }
+
   /* every status has a message */
   for (int s = EP_ERR_HIP; s <= EP_OK; ++s)
     expect(ep_status_string(s) != NULL && strlen(ep_status_string(s)) > 0, "status string");

@@ -122,3 +122,57 @@ def test_argument_errors_return_before_launch():
     ro = ep.CRecv(base16, base16, rows)
     assert lib.ep_messages_unpack(ctypes.byref(pm.c()), ctypes.byref(cm), base16, 64, None,
                                   ctypes.byref(ro), base16, base16, base16, None) == -1
+
+
+def _oracle_sizes(R, T, H, E, K, quant, rb, topk):
+    """Arena bytes and descriptor count as the oracle's packer lays them
+    out (a pass with no room writes nothing but reports both)."""
+    from combine_ep_get_layout_amd import inputs
+    from oracle import oracle as orc
+    pm = orc.Problem(R, T, H, E, K, mode=orc.MODE_MSG, quant=quant, region_bytes=rb)
+    w = inputs.small("sz", R=R, T=T, H=H, E=E, K=K, mode=orc.MODE_MSG, quant=quant, seed=1)
+    x, wt = inputs.gen_x(w), inputs.gen_weights(w)
+    m = orc.messages(pm, x, topk, wt, 0, 0)
+    counts = orc.layout(pm, topk).num_tokens_per_rank
+    return counts, (int(m.arena_base[0][-1]), int(m.arena_base[1][-1]), m.num_desc)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_message_sizes_match_the_oracle(seed):
+    """ep_messages_capacity with the read-back counts equals the oracle's
+    arena bytes and descriptor count exactly; without counts it bounds them.
+    Region sizes from 16 bytes up force pieces on both sides of every put."""
+    from combine_ep_get_layout_amd import inputs
+    g = np.random.default_rng(900 + seed)
+    R = int(g.choice([1, 2, 3, 5, 8]))
+    E = R * int(g.integers(1, 5))
+    K = int(g.integers(1, min(E, 6) + 1))
+    T = int(g.integers(0, 40))
+    quant = int(g.integers(0, 3))
+    H = 128 * int(g.integers(1, 4))
+    rb = 16 * int(g.choice([1, 2, 3, 7, 64, 1000, 1 << 17]))
+    w = inputs.small("sz", R=R, T=T, H=H, E=E, K=K, mode=ep.MODE_MESSAGES, quant=quant, seed=seed)
+    topk = inputs.gen_topk(w)
+    if T and seed % 3 == 0:
+        topk = inputs.masked_topk(w, topk, 0.3, 0.3 if K > 1 else 0.0, seed=seed)
+    counts, want = _oracle_sizes(R, T, H, E, K, quant, rb, topk)
+    p = ep.Problem(R, T, H, E, K, mode=ep.MODE_MESSAGES, quant=quant, region_bytes=rb)
+    assert ep.messages_sizes(p, counts) == want
+    worst = ep.messages_sizes(p)
+    assert all(a >= b for a, b in zip(worst, want)), (worst, want)
+    # routing every token to every rank (possible when K >= R: entry k goes
+    # to rank k % R) reaches the arena bound exactly
+    if T and K >= R:
+        k = np.arange(K)
+        full = np.broadcast_to(((k % R) * (E // R) + (k // R) % (E // R)).astype(np.int32),
+                               (R, T, K)).copy()
+        _, wf = _oracle_sizes(R, T, H, E, K, quant, rb, full)
+        assert wf[:2] == worst[:2] and wf[2] <= worst[2]
+
+
+def test_message_sizes_reject_bad_counts():
+    p = ep.Problem(2, 4, 128, 4, 2, mode=ep.MODE_MESSAGES, quant=1, region_bytes=256)
+    with pytest.raises(ep.EPError):
+        ep.messages_sizes(p, np.array([[0, 5], [1, 1]]))  # 5 > T
+    with pytest.raises(ep.EPError):
+        ep.messages_sizes(ep.Problem(2, 4, 128, 4, 2), None)  # not message mode

@@ -23,6 +23,20 @@ CASES = [
     ("ll_bf16_dups", 4, 200, 128, 8, 8, L, 0, 1, 0.1, 0.4),
     ("experts_over_tokens", 2, 110, 128, 2048, 64, N, 0, 1, 0.0, 0.0),
     ("ll_experts_over_tokens", 2, 100, 128, 1024, 40, L, QF, 1, 0.0, 0.0),
+    # every FP8 row split the normal-mode launcher picks, fused: one
+    # wavefront of one pair per lane (hidden 1024), four wavefronts of one
+    # pair (2048), one wavefront of four pairs (4096: the training shape's
+    # kernel), twelve wavefronts of two pairs (20480); both scale forms,
+    # alignment, masked and duplicate ids
+    ("fp8_h1024_one_wave_ue8", 4, 600, 1024, 32, 8, N, QU, 4, 0.1, 0.2),
+    ("fp8_h1024_one_wave_f32", 4, 600, 1024, 32, 8, N, QF, 2, 0.05, 0.0),
+    ("fp8_h2048_four_waves_f32", 4, 300, 2048, 32, 8, N, QF, 8, 0.1, 0.2),
+    ("fp8_h2048_four_waves_ue8", 4, 300, 2048, 32, 8, N, QU, 1, 0.0, 0.0),
+    ("fp8_h4096_four_pairs_ue8", 4, 300, 4096, 32, 8, N, QU, 8, 0.1, 0.2),
+    ("fp8_h4096_four_pairs_f32", 4, 300, 4096, 32, 8, N, QF, 2, 0.05, 0.1),
+    ("fp8_h20480_two_pairs_f32", 2, 400, 20480, 16, 8, N, QF, 4, 0.1, 0.1),
+    ("fp8_h20480_two_pairs_ue8", 2, 400, 20480, 16, 8, N, QU, 1, 0.0, 0.2),
+    ("ll_fp8_h4096_ue8", 4, 200, 4096, 32, 8, L, QU, 1, 0.1, 0.0),
 ]
 
 
@@ -92,9 +106,15 @@ def test_fused_equals_separate_calls_and_oracle(c):
     assert torch.equal(rf.x[rows], rs.x[rows])
     _, orecv, osc = orc.dispatch(po, x, topk, ol.send_pos, cap)
     g = h(rf.x.view(torch.uint16) if quant == 0 else rf.x)
-    assert np.array_equal(g[rows.cpu().numpy()], orecv[rows.cpu().numpy()])
+    rn = rows.cpu().numpy()
+    assert np.array_equal(g[rn], orecv[rn])
     if quant:
         assert torch.equal(rf.scales, rs.scales)
+        G, RT = H // 128, R * T
+        gi = np.arange(G)
+        si = ((rn[:, None] // RT * G + gi) * RT + rn[:, None] % RT if mode == L
+              else gi[None, :] * cap + rn[:, None]).reshape(-1)
+        assert np.array_equal(h(rf.scales)[si], osc[si])
 
 
 @pytest.mark.parametrize("name", ["ll_decode", "normal_prefill"])
@@ -131,3 +151,53 @@ def test_fused_workload(name):
         gi = torch.arange(G, device=DEV)
         si = ((rows // RT)[:, None] * G + gi[None, :]) * RT + (rows % RT)[:, None]
         assert torch.equal(rf.scales[si.reshape(-1)], rs.scales[si.reshape(-1)])
+
+
+def test_fused_workload_fp8_train():
+    """The FP8 training shape (16 x 8192 tokens, hidden 4096, 128 experts,
+    top-8 Zipf(1.0), outlier channels, UE8M0 scales) through the fused call,
+    in the launch configuration the bench times (one wavefront of four pairs
+    per lane): every layout output against the oracle; every code row and
+    the whole column-major scale array against the separate calls; 1,024
+    sampled tokens' codes and scales in all their rows against the oracle."""
+    w = inputs.WORKLOADS["fp8_train"]
+    say("fused workload fp8_train: inputs")
+    topk, x = inputs.gen_topk(w), inputs.gen_x(w)
+    p = ep.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+    po = orc.Problem(w.R, w.T, w.H, w.E, w.K, mode=w.mode, quant=w.quant)
+    ol = orc.layout(po, topk)
+    cap = ol.total_rows
+    tk = torch.from_numpy(topk).to(DEV)
+    xg = torch.from_numpy(x).view(torch.bfloat16).to(DEV)
+    lf = ep.Layout(p, recv_capacity=cap)
+    rf = ep.Recv(p, cap)
+    rf.scales.fill_(0x5A)
+    say("fused workload fp8_train: fused call")
+    ep.dispatch_fused(p, tk, lf, xg, rf, ep.workspace(p))
+    torch.cuda.synchronize()
+    assert_layout_equal(lf, ol, w.mode)
+    say("fused workload fp8_train: separate calls")
+    ls = ep.Layout(p, recv_capacity=cap)
+    rs = ep.Recv(p, cap)
+    rs.scales.fill_(0x5A)
+    wss = ep.workspace(p)
+    ep.get_layout(p, tk, ls, wss)
+    ep.dispatch(p, ls, xg, recv=rs, ws=wss)
+    torch.cuda.synchronize()
+    assert int(h(ls.err)[0]) == 0
+    step = 1 << 14
+    for a in range(0, cap, step):
+        assert torch.equal(rf.x[a:a + step], rs.x[a:a + step]), a
+    assert torch.equal(rf.scales, rs.scales)
+    say("fused workload fp8_train: sampled tokens against the oracle")
+    toks = np.sort(np.random.default_rng(5).choice(w.N, 1024, replace=False))
+    sub = orc.Problem(1, toks.size, w.H, 1, 1, quant=w.quant)
+    _, codes, scales = orc.dispatch(sub, x.reshape(-1, w.H)[toks], np.zeros((1, toks.size, 1), np.int32),
+                                    np.arange(toks.size, dtype=np.int32), toks.size)
+    sp = ol.send_pos.reshape(-1, w.K)[toks]
+    for k in range(w.K):
+        rows = sp[:, k].astype(np.int64)
+        assert np.array_equal(h(rf.x[torch.from_numpy(rows).to(DEV)]), codes), k
+        for g in range(w.G):
+            got = h(rf.scales[torch.from_numpy(g * cap + rows).to(DEV)])
+            assert np.array_equal(got, scales[g * toks.size:(g + 1) * toks.size]), (k, g)

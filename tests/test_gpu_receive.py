@@ -30,6 +30,9 @@ CASES = [
     ("r16_many_local", 16, 24, 256, 512, 6, ep.QUANT_FP8_F32, 1024, 0.0, 0.0),
     ("r4_bf16_dups", 4, 33, 128, 8, 8, ep.QUANT_NONE, 128, 0.1, 0.4),
     ("r256", 256, 2, 128, 256, 4, ep.QUANT_FP8_F32, 4096, 0.0, 0.0),  # the rank limit
+    # a 1,240,832-byte arena in 38,776 regions of 32 bytes: region indices
+    # near the 16-bit key limit, one descriptor per 32 bytes
+    ("r1_1mib_arena_32b_regions", 1, 600, 1024, 2, 2, ep.QUANT_NONE, 32, 0.0, 0.0),
 ]
 FILL = 0x5C
 
@@ -169,6 +172,49 @@ def test_execute_rejects_corrupt_descriptor_like_the_oracle():
     e, oarena = orc.messages_execute(po, om, recv_cap, np.full(recv_cap + 64, 0xA5, np.uint8))
     assert e == orc.ERR_MESSAGE and int(h(err2)[0]) == ep.DEVERR_MESSAGE
     assert np.array_equal(h(arena2), oarena)
+
+
+def test_region_index_past_16_bits_is_rejected_like_the_oracle():
+    """The same 1,240,832-byte arena in 16-byte regions (77,552 of them): a
+    key's 16-bit region index cannot name the pieces past region 65535, so
+    the packer writes them with all-ones keys and raises the capacity bit;
+    delivery rejects them (no such rank: the message bit) and leaves their
+    bytes, the flag among them, undelivered; the receiver then finds no
+    flag and skips the message.  Every descriptor, the error words, the
+    receive arena and the unpacked buffers equal the oracle's."""
+    R, T, H, E, K, rb = 1, 600, 1024, 2, 2, 16
+    w = inputs.small("recv_rb16", R=R, T=T, H=H, E=E, K=K, mode=ep.MODE_MESSAGES,
+                     quant=ep.QUANT_NONE, seed=61, region_bytes=rb, epoch=5)
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    say("receive: 16-byte regions over 1 MiB")
+    gl, ws = gpu_layout(p, topk)
+    send_cap, desc_cap = ep.messages_capacity(p, h(gl.num_tokens_per_rank))
+    assert send_cap == 1240832 and desc_cap == 1240832 // 16
+    msgs = ep.Messages(p, send_cap, desc_cap)
+    ep.dispatch(p, gl, torch.from_numpy(x).view(torch.bfloat16).to(DEV), msgs=msgs,
+                topk_idx=torch.from_numpy(topk).to(DEV), topk_weights=torch.from_numpy(wt).to(DEV),
+                ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(gl.err)[0]) == ep.DEVERR_CAPACITY
+    om = orc.messages(po, x, topk, wt, send_cap, desc_cap)
+    assert om.err == orc.ERR_CAPACITY and om.num_desc == desc_cap
+    assert np.array_equal(h(msgs.descriptors), om.desc)
+    assert np.array_equal(h(msgs.send_arena), om.send_arena)
+    arena = torch.full((send_cap + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_execute(p, msgs, arena[:send_cap], err)
+    out, cnt, src = ep.unpack_buffers(p)
+    out.x.view(torch.uint8).fill_(FILL)
+    ep.messages_unpack(p, msgs, arena[:send_cap], gl.num_tokens_per_expert, out, cnt, src, err)
+    torch.cuda.synchronize()
+    e1, oarena = orc.messages_execute(po, om, send_cap, np.full(send_cap + 64, 0xA5, np.uint8))
+    assert e1 == orc.ERR_MESSAGE
+    u = orc.messages_unpack(po, oarena[:send_cap], om.table, h(gl.num_tokens_per_expert),
+                            fill_codes=FILL)
+    assert int(h(err)[0]) == (e1 | u.err) == ep.DEVERR_MESSAGE
+    assert np.array_equal(h(arena), oarena)
+    compare_unpacked(w, out, cnt, src, u)
 
 
 def test_workload_messages_delivery_and_unpack():

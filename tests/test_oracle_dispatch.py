@@ -131,3 +131,45 @@ def test_identity_dequant_is_exact_for_pow2_scales():
         for g in range(w.G):
             deq[r, g * 128:(g + 1) * 128] *= np.float32(2.0 ** (int(scales[g * cap + r]) - 127))
     assert np.array_equal(bf16_to_f32(y), deq)
+
+
+@pytest.mark.parametrize("mode", [orc.MODE_NORMAL, orc.MODE_LL])
+def test_dequant_fp32_scales_round_the_exact_product_once(mode):
+    """The identity expert for fp32 scales: y = bf16(decode(code) * scale),
+    the product exact (a 4-bit code times a 24-bit scale) and rounded once,
+    to nearest even.  Checked against the exact rational product of
+    PyTorch's float8_e4m3fn decode and the fp32 scale, rounded by integer
+    arithmetic, for every finite code, scales from 2^-30 to 2^10 (bf16
+    subnormal products included) and short dyadic scales whose products
+    fall exactly halfway between two bf16 numbers; scales read at their
+    column-major place of each layout."""
+    from fractions import Fraction
+
+    from test_oracle_codecs import _bf16_exact
+
+    R, T, H, E, K = 2, 4, 256, 4, 2
+    G = H // 128
+    p = orc.Problem(R, T, H, E, K, mode=mode, quant=orc.Q_FP8_F32)
+    cap = 12 if mode == orc.MODE_NORMAL else E * R * T
+    rng = np.random.default_rng(17)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    codes = rng.choice(finite, (cap, H)).astype(np.uint8)
+    codes[0, :finite.size] = finite
+    codes[1, :finite.size] = finite[::-1]
+    nsc = G * (cap if mode == orc.MODE_NORMAL else E * R * T)
+    scales = np.exp2(rng.uniform(-30, 10, nsc)).astype(np.float32)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, 1.5, 2.0 ** -20 * (1 + 2.0 ** -5),
+                     np.float32(1e-4) / np.float32(448.0), 1.0], np.float32)
+    scales[:ties.size] = ties
+    rows = np.arange(cap, dtype=np.int32)[::-1].copy()
+    y = orc.dequant_rows(p, codes, scales, cap, rows)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    RT = R * T
+    for i, r in enumerate(rows.tolist()):
+        for g in range(G):
+            si = g * cap + r if mode == orc.MODE_NORMAL else ((r // RT) * G + g) * RT + r % RT
+            sc = Fraction(float(scales[si]))
+            # a zero code keeps its sign (IEEE: -0 times a positive scale is -0)
+            want = [_bf16_exact(Fraction(float(v)) * sc) if v != 0 else
+                    (0x8000 if np.signbit(v) else 0) for v in dec[r, g * 128:(g + 1) * 128]]
+            assert y[i, g * 128:(g + 1) * 128].tolist() == want, (r, g)

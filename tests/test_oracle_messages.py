@@ -92,8 +92,10 @@ def brute_messages(p, x, topk, wts):
                 la, ra, rem = so + off, ro + off, ln
                 while rem:
                     c = min(rem, RB - la % RB, RB - ra % RB)
-                    descs.append((wqe, s * R + d, ra, (d << 16) | (ra // RB), c,
-                                  (s << 16) | (la // RB), la))
+                    rkey, lkey = (d << 16) | (ra // RB), (s << 16) | (la // RB)
+                    if la // RB > 0xFFFF or ra // RB > 0xFFFF:  # index past 16 bits
+                        rkey = lkey = 0xFFFFFFFF
+                    descs.append((wqe, s * R + d, ra, rkey, c, lkey, la))
                     wqe += 1
                     la += c
                     ra += c
@@ -147,6 +149,29 @@ def test_messages_brute_force(case, seed):
             assert m.send_arena[so:so + len(reg)].tobytes() == reg, (s, d)
     assert m.num_desc == len(descs)
     assert [parse_desc(bytes(d)) for d in m.desc] == descs
+
+
+@pytest.mark.parametrize("RB,poisoned", [(16, True), (32, False)])
+def test_region_index_past_16_bits(RB, poisoned):
+    """Keys hold a region index in 16 bits.  One rank sending 600 bf16 rows of
+    hidden 1024 to itself fills a 1,240,832-byte arena: 77,552 regions of 16
+    bytes (pieces past region 65535 cannot be named: their keys are all ones,
+    a rank no problem has, and the capacity bit is raised) or 38,776 regions
+    of 32 bytes (every key fits).  The brute force applies the same rule."""
+    R, T, H, E, K = 1, 600, 1024, 2, 2
+    w = inputs.small(R=R, T=T, H=H, E=E, K=K, mode=orc.MODE_MSG, quant=orc.Q_NONE, seed=3)
+    topk, x, wts = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p = orc.Problem(R, T, H, E, K, mode=orc.MODE_MSG, quant=orc.Q_NONE, region_bytes=RB, epoch=9)
+    regions, offs, sb, rb, descs = brute_messages(p, x, topk, wts)
+    assert len(regions[(0, 0)]) == 1240832
+    m = orc.messages(p, x, topk, wts, send_cap=sb[-1], desc_cap=len(descs))
+    assert m.err == (orc.ERR_CAPACITY if poisoned else 0)
+    got = [parse_desc(bytes(d)) for d in m.desc]
+    assert got == descs
+    bad = [q for q in got if q[3] == 0xFFFFFFFF]
+    assert all(q[5] == 0xFFFFFFFF and q[6] // RB > 0xFFFF for q in bad)
+    assert len(bad) == (1240832 // 16 - 65536 if poisoned else 0)  # regions 65536 .. 77551
+    assert m.send_arena[:len(regions[(0, 0)])].tobytes() == regions[(0, 0)]
 
 
 @pytest.mark.parametrize("RB", [2 << 20, 64 << 10])
