@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ep.h"
 #include "ep_internal.hpp"
 #include "msg_format.hpp"
@@ -222,6 +224,7 @@ const char* ep_status_string(int s) {
     case EP_ERR_WORKSPACE: return "workspace too small";
     case EP_ERR_CAPACITY: return "capacity too small";
     case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_SCRATCH: return "problem needs more scratch than the fixed no-alloc array";
     default: return "unknown status";
   }
 }
@@ -539,3 +542,56 @@ int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// ep_dispatch_fused_noalloc: ep_dispatch_fused with the library's own fixed
+// scratch array in place of the caller's workspace, for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy of the array
+// (EP_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code the
+// array's name is only a stand-in for the symbol: its device address on each
+// GPU is looked up once, with that GPU current, and cached; kernels receive
+// that address as their workspace.
+
+static __device__ __align__(256) uint8_t scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (first call on a device: one
+// hipGetSymbolAddress with that device current, the caller's current device
+// restored afterwards).
+int scratch_on_device(int dev, void** out) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return EP_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return EP_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return EP_ERR_HIP;
+    if (e != hipSuccess || !p) return EP_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" int ep_dispatch_fused_noalloc(const ep_problem* p, const int32_t* topk_idx,
+                                         const ep_layout* layout, const uint16_t* x,
+                                         const ep_recv* recv, void* stream) {
+  Geometry g;
+  const int st = ep::make_geometry(p, &g);
+  if (st != EP_OK) return st;
+  if (g.ws_bytes > (size_t)EP_NOALLOC_SCRATCH_BYTES) return EP_ERR_SCRATCH;
+  int dev = 0;
+  const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return EP_ERR_HIP;
+  void* ws = nullptr;
+  const int sst = scratch_on_device(dev, &ws);
+  if (sst != EP_OK) return sst;
+  return ep_dispatch_fused(p, topk_idx, layout, x, recv, ws, (size_t)EP_NOALLOC_SCRATCH_BYTES,
+                           stream);
+}

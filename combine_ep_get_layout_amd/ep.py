@@ -22,8 +22,10 @@ QUANT_NONE, QUANT_FP8_F32, QUANT_FP8_UE8M0 = 0, 1, 2
 DEVERR_TOPK_RANGE, DEVERR_LL_OVERFLOW, DEVERR_CAPACITY, DEVERR_MESSAGE = 1, 2, 4, 8
 
 EXPORTS = ["ep_workspace_bytes", "ep_max_recv_rows", "ep_messages_capacity", "ep_get_layout",
-           "ep_dispatch", "ep_dispatch_fused", "ep_combine", "ep_messages_execute",
-           "ep_messages_unpack", "ep_status_string"]
+           "ep_dispatch", "ep_dispatch_fused", "ep_dispatch_fused_noalloc", "ep_combine",
+           "ep_messages_execute", "ep_messages_unpack", "ep_status_string"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # EP_NOALLOC_SCRATCH_BYTES
+ERR_SCRATCH = -8
 
 
 class EPError(RuntimeError):
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
         l.ep_dispatch_fused.argtypes = [P, _vp, ctypes.POINTER(CLayout), _vp,
                                         ctypes.POINTER(CRecv), _vp, ctypes.c_size_t, _vp]
         l.ep_dispatch_fused.restype = ctypes.c_int
+        l.ep_dispatch_fused_noalloc.argtypes = [P, _vp, ctypes.POINTER(CLayout), _vp,
+                                                ctypes.POINTER(CRecv), _vp]
+        l.ep_dispatch_fused_noalloc.restype = ctypes.c_int
         l.ep_combine.argtypes = [P, ctypes.POINTER(CLayout), _vp, ctypes.c_int64, _vp, _vp, _vp]
         l.ep_combine.restype = ctypes.c_int
         l.ep_messages_execute.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64, _vp,
@@ -341,6 +346,33 @@ def dispatch_fused(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.
     _check(lib().ep_dispatch_fused(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl), _ptr(x),
                                    ctypes.byref(cr), _ptr(ws), ws.numel(), _stream(stream)),
            "ep_dispatch_fused")
+
+
+def dispatch_fused_noalloc(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
+                           recv: Recv, stream=None) -> None:
+    """dispatch_fused with the library's fixed scratch array instead of a
+    workspace (ep_dispatch_fused_noalloc): nothing is allocated."""
+    R, T, H, E, K = p.R, p.T, p.H, p.E, p.K
+    _need(p.mode in (MODE_NORMAL, MODE_LOW_LATENCY), "normal or low-latency problem")
+    _need(topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32")
+    _need(layout.num_tokens_per_expert.numel() == R * E and layout.is_token_in_rank.numel() == R * T * R,
+          "layout buffers do not match the problem")
+    _need(layout.send_pos is not None and layout.send_pos.numel() == R * T * K, "send_pos [R][T][K]")
+    _need(layout.send_head is None or layout.send_head.numel() == R * T * R, "send_head [R][T][R]")
+    _need(layout.recv_src_idx is None or layout.recv_src_idx.numel() >= layout.recv_capacity,
+          "recv_src_idx smaller than recv_capacity")
+    _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
+    _need(recv.x.shape[0] >= recv.capacity and recv.x.shape[1] == H, "recv x [capacity][H]")
+    if p.quant != QUANT_NONE:
+        n = p.G * (E * R * T if p.mode == MODE_LOW_LATENCY else recv.capacity)
+        _need(recv.scales is not None and recv.scales.numel() >= n, "recv scales")
+        _need(recv.x.element_size() == 1, "FP8 codes are bytes")
+    else:
+        _need(recv.x.element_size() == 2, "bf16 rows")
+    cl, cr = layout.c(), recv.c()
+    _check(lib().ep_dispatch_fused_noalloc(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl),
+                                           _ptr(x), ctypes.byref(cr), _stream(stream)),
+           "ep_dispatch_fused_noalloc")
 
 
 def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,

@@ -82,6 +82,11 @@ extern "C" {
 #define EP_ERR_WORKSPACE (-5)   /* workspace smaller than ep_workspace_bytes */
 #define EP_ERR_CAPACITY (-6)    /* a capacity that is too small on its face */
 #define EP_ERR_HIP (-7)         /* the HIP runtime reported a launch error */
+#define EP_ERR_SCRATCH (-8)     /* ep_dispatch_fused_noalloc: the problem needs more scratch
+                                   than EP_NOALLOC_SCRATCH_BYTES */
+
+/* size of the library's fixed scratch array (ep_dispatch_fused_noalloc) */
+#define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* device error word bits */
 #define EP_DEVERR_TOPK_RANGE 1  /* a topk_idx entry outside [-1, E): entry skipped */
@@ -242,6 +247,25 @@ int ep_dispatch(const ep_problem* p, const ep_layout* layout, const uint16_t* x,
 int ep_dispatch_fused(const ep_problem* p, const int32_t* topk_idx, const ep_layout* layout,
                       const uint16_t* x, const ep_recv* recv, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* ep_dispatch_fused without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid allocation.  Calls no hipMalloc / hipFree and no allocating
+ * routine.  Its scratch memory is a fixed array of EP_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library: each GPU the library is loaded on holds its
+ * own copy until the process ends.  A problem whose ep_workspace_bytes
+ * exceeds that size returns EP_ERR_SCRATCH before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls whose work
+ * may overlap on one GPU -- streams with no ordering between them, or host
+ * threads enqueueing concurrently onto different streams -- race and give
+ * wrong results; calls ordered on one stream are safe.  The first call on
+ * a GPU looks up the array's device address (hipGetSymbolAddress with that
+ * GPU current, the caller's current device restored); `stream`'s device
+ * decides which GPU.  Arguments and results otherwise as ep_dispatch_fused. */
+int ep_dispatch_fused_noalloc(const ep_problem* p, const int32_t* topk_idx,
+                              const ep_layout* layout, const uint16_t* x, const ep_recv* recv,
+                              void* stream);
 
 /* Combine ("DeepEP" sec. 2.3: the handle walked backwards): out[s][t] =
  * bf16( sum_k topk_weights[s][t][k] * y[send_pos[s][t][k]] ), accumulated in

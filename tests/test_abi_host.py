@@ -66,7 +66,7 @@ def test_problem_validation(kw, ok):
 
 
 def test_status_strings():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert ep.status_string(s) != "unknown status"
     assert ep.status_string(-99) == "unknown status"
 
