@@ -62,32 +62,48 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def layout_bytes(w, rows_written):
-    """topk read, send_pos / is_token_in_rank / send_head written, and one
-    recv_src_idx entry per filled row."""
+def layout_rw(w, rows_written):
+    """(read, written) bytes: topk read; send_pos / is_token_in_rank /
+    send_head written, and one recv_src_idx entry per filled row."""
     R, T, K = w.R, w.T, w.K
     M = R * T * K
-    b = 4 * M + R * T * R + 4 * R * T * R + 4 * rows_written
+    wr = R * T * R + 4 * R * T * R + 4 * rows_written
     if w.mode != 2:
-        b += 4 * M
-    return b
+        wr += 4 * M
+    return 4 * M, wr
 
 
-def dispatch_bytes(w, rows=None):
+def dispatch_rw(w, rows=None):
+    """(read, written) bytes: x read once and a slot per routed pair; the
+    rows (bf16, or codes and scales) written."""
     R, T, H, K, G = w.R, w.T, w.H, w.K, w.G
     N, M = R * T, R * T * K
     row = {0: 2 * H, 1: H + 4 * G, 2: H + G}[w.quant]
     if w.mode == 3:  # rank-major: one row per (token, rank), plus its top-k ids and weights
-        return 2 * H * N + rows * (row + 8 * K) + 4 * M + 8 * M
-    return 2 * H * N + row * M + 4 * M
+        return 2 * H * N + 4 * M + 8 * M, rows * (row + 8 * K)
+    return 2 * H * N + 4 * M, row * M
 
 
-def combine_bytes(w, rows=None):
+def combine_rw(w, rows=None):
+    """(read, written) bytes: the routed rows, slots and weights read; the
+    output written."""
     R, T, H, K = w.R, w.T, w.H, w.K
     N, M = R * T, R * T * K
     if w.mode == 3:  # rank-major: each distinct row once, unweighted
-        return 2 * H * rows + 2 * H * N + 4 * M
-    return 2 * H * M + 2 * H * N + 8 * M
+        return 2 * H * rows + 4 * M, 2 * H * N
+    return 2 * H * M + 8 * M, 2 * H * N
+
+
+def layout_bytes(w, rows_written):
+    return sum(layout_rw(w, rows_written))
+
+
+def dispatch_bytes(w, rows=None):
+    return sum(dispatch_rw(w, rows))
+
+
+def combine_bytes(w, rows=None):
+    return sum(combine_rw(w, rows))
 
 
 # sources each profiled kernel is built from (its counters go stale when
@@ -174,16 +190,23 @@ class Runner:
             self.recv_arena = torch.empty(self.recv_cap, dtype=torch.uint8, device=dev)
             self.err = torch.zeros(1, dtype=torch.int32, device=dev)
             self.unp = ep.unpack_buffers(self.p)
-            lay = layout_bytes(w, 0)
-            disp = 2 * w.H * w.N + 8 * w.K * w.N + msg_bytes + 64 * nd + 64 * w.R * w.R
             cb = 2 if w.quant == ep.QUANT_NONE else 1
             sb = {0: 0, 1: 4, 2: 1}[w.quant]
             routed = int((topk >= 0).sum())
             tokens_sent = int(table[:, :, 3].sum())
-            execute = 2 * msg_bytes + 64 * nd
-            unpack = (routed * (2 * (w.H * cb + w.G * sb) + 4) + tokens_sent * (4 * w.K + 4)
-                      + 32 * n_msg)
-            self.bytes = {"layout": lay, "dispatch": disp, "execute": execute, "unpack": unpack}
+            row = w.H * cb + w.G * sb
+            # (read, written): the packer reads x, the weights and the ids
+            # and writes the messages, descriptors and table; delivery reads
+            # the descriptors and copies the messages; the receiver reads
+            # each routed row, the per-token metadata, header and flag, and
+            # writes the rows, scales and source indices
+            self.rw = {"layout": layout_rw(w, 0),
+                       "dispatch": (2 * w.H * w.N + 8 * w.K * w.N,
+                                    msg_bytes + 64 * nd + 64 * w.R * w.R),
+                       "execute": (msg_bytes + 64 * nd, msg_bytes),
+                       "unpack": (routed * row + tokens_sent * (4 * w.K + 4) + 32 * n_msg,
+                                  routed * (row + 4))}
+            self.bytes = {k: sum(v) for k, v in self.rw.items()}
             # the pack and delivery calls are several launches each
             self.kernels = {"unpack": "msg_unpack"}
             self.extra = {"messages": n_msg, "descriptors": nd, "message_bytes": msg_bytes}
@@ -203,49 +226,53 @@ class Runner:
             self.y = torch.empty((self.rows, w.H), dtype=torch.bfloat16, device=dev)
             self.y.normal_()
         self.out = torch.empty((w.R, w.T, w.H), dtype=torch.bfloat16, device=dev)
-        self.bytes = {"layout": layout_bytes(w, filled), "dispatch": dispatch_bytes(w, self.rows),
-                      "combine": combine_bytes(w, self.rows)}
+        self.rw = {"layout": layout_rw(w, filled), "dispatch": dispatch_rw(w, self.rows),
+                   "combine": combine_rw(w, self.rows)}
+        self.bytes = {k: sum(v) for k, v in self.rw.items()}
         self.kernels = {"combine": "combine_rows"}
         # normal-mode FP8 dispatch also launches the scale transpose
         if w.quant == ep.QUANT_NONE or w.mode == ep.MODE_LOW_LATENCY:
             self.kernels["dispatch"] = "dispatch_copy" if w.quant == 0 else "dispatch_fp8"
         if self.fused:  # the fused call launches the layout's kernels too
-            lb = self.bytes.pop("layout")
-            self.bytes = {"layout+dispatch": lb + self.bytes["dispatch"],
-                          "combine": self.bytes["combine"]}
+            (lr, lw), (dr, dw) = self.rw["layout"], self.rw["dispatch"]
+            self.rw = {"layout+dispatch": (lr + dr, lw + dw), "combine": self.rw["combine"]}
+            self.bytes = {k: sum(v) for k, v in self.rw.items()}
             self.kernels = {"combine": "combine_rows"}
         self.extra = {}
 
     def phases(self):
-        """The step's calls in order, one per timed phase (built once)."""
+        """The step's calls in order, one per timed phase, each checked and
+        marshalled once (ep.prepare): a call in the timed loop only hands
+        the cached arguments to the library, as a C caller would."""
         if getattr(self, "_phases", None) is not None:
             return self._phases
         ep, p = self.ep, self.p
-        ph = [("layout", lambda: ep.get_layout(p, self.topk, self.lay, self.ws))]
+        ph = [("layout", ep.prepare(ep.get_layout, p, self.topk, self.lay, self.ws))]
         if self.msgs is not None:
-            ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, msgs=self.msgs,
-                                                       topk_idx=self.topk, topk_weights=self.wt,
-                                                       ws=self.ws)))
-            ph.append(("execute", lambda: ep.messages_execute(p, self.msgs, self.recv_arena,
-                                                              self.err)))
-            ph.append(("unpack", lambda: ep.messages_unpack(p, self.msgs, self.recv_arena,
-                                                            self.lay.num_tokens_per_expert,
-                                                            *self.unp, self.err)))
+            ph.append(("dispatch", ep.prepare(ep.dispatch, p, self.lay, self.x, msgs=self.msgs,
+                                              topk_idx=self.topk, topk_weights=self.wt,
+                                              ws=self.ws)))
+            ph.append(("execute", ep.prepare(ep.messages_execute, p, self.msgs, self.recv_arena,
+                                             self.err)))
+            ph.append(("unpack", ep.prepare(ep.messages_unpack, p, self.msgs, self.recv_arena,
+                                            self.lay.num_tokens_per_expert, *self.unp,
+                                            self.err)))
         elif self.fused:  # layout and dispatch in one call
-            ph = [("layout+dispatch", lambda: ep.dispatch_fused(p, self.topk, self.lay, self.x,
-                                                                self.recv, self.ws)),
-                  ("combine", lambda: ep.combine(p, self.lay, self.y, self.wt, self.out))]
+            ph = [("layout+dispatch", ep.prepare(ep.dispatch_fused, p, self.topk, self.lay,
+                                                 self.x, self.recv, self.ws)),
+                  ("combine", ep.prepare(ep.combine, p, self.lay, self.y, self.wt, self.out))]
         else:
             if self.w.mode == ep.MODE_RANK_MAJOR:  # rows plus their top-k metadata
-                ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
-                                                           topk_idx=self.topk,
-                                                           topk_weights=self.wt, ws=self.ws)))
-                ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, None, self.out)))
+                ph.append(("dispatch", ep.prepare(ep.dispatch, p, self.lay, self.x, recv=self.recv,
+                                                  topk_idx=self.topk, topk_weights=self.wt,
+                                                  ws=self.ws)))
+                ph.append(("combine", ep.prepare(ep.combine, p, self.lay, self.y, None,
+                                                 self.out)))
             else:
-                ph.append(("dispatch", lambda: ep.dispatch(p, self.lay, self.x, recv=self.recv,
-                                                           ws=self.ws)))
-                ph.append(("combine", lambda: ep.combine(p, self.lay, self.y, self.wt,
-                                                         self.out)))
+                ph.append(("dispatch", ep.prepare(ep.dispatch, p, self.lay, self.x,
+                                                  recv=self.recv, ws=self.ws)))
+                ph.append(("combine", ep.prepare(ep.combine, p, self.lay, self.y, self.wt,
+                                                 self.out)))
         self._phases = ph
         return ph
 
@@ -304,6 +331,28 @@ class Runner:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
+    def publish_curve(self, reps=20, batches=(0, 1, 4, 32)):
+        """Delivery time (ms, mean of `reps` back-to-back calls, events
+        around them) for each publication batch: 0 = every flag after a
+        second launch; B = flags released every B messages per workgroup."""
+        torch, ep = self.torch, self.ep
+        out = {}
+        for b in batches:
+            call = ep.prepare(ep.messages_execute, self.p, self.msgs, self.recv_arena, self.err,
+                              publish_batch=b)
+            call()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                call()
+            e.record()
+            torch.cuda.synchronize()
+            out[str(b)] = round(s.elapsed_time(e) / reps, 4)
+        if int(self.err.item()):
+            raise RuntimeError(f"device error word {int(self.err.item())}")
+        return out
+
     def run_cold(self, steps, flush_bytes=1 << 30):
         """Step times with the last-level cache flushed before every step
         (a 1 GiB buffer overwritten, untimed); events bracket each step."""
@@ -321,7 +370,7 @@ class Runner:
         del scratch
         return t
 
-    def report(self, steps, warmup, extra=True):
+    def report(self, steps, warmup, extra=True, probes=None):
         w = self.w
         log(f"[bench] {w.name}: timing {steps} steps after {warmup} warm-up")
         ms, ph = self.run(steps, warmup)
@@ -361,6 +410,20 @@ class Runner:
         }
         if traffic is not None:  # counted HBM bytes over the same launch time
             res["roofline"]["traffic_GBps"] = round(traffic / (mean_ph[dom] * 1e-3) / 1e9, 1)
+        if probes is not None:
+            # the same reads and writes at the probes' read-only and
+            # write-only rates, taking turns: the measured roof for this mix
+            for k in phases:
+                phases[k]["frac_of_mix_ceiling"] = round(mix_ceiling(self.rw[k], probes)
+                                                         / mean_ph[k], 4)
+            rd = sum(r for r, _ in self.rw.values())
+            wr = sum(x for _, x in self.rw.values())
+            at = sum(mix_ceiling(v, probes) for v in self.rw.values())
+            res["mix_ceiling"] = {"read_bytes": rd, "written_bytes": wr,
+                                  "ms_at_probe_roofs": round(at, 4),
+                                  "GBps": round(total / (at * 1e-3) / 1e9, 1),
+                                  "frac": round(at / ms, 4)}
+            res["roofline"]["frac_of_mix_ceiling"] = phases[dom]["frac_of_mix_ceiling"]
         # the calls after the layout alone (the bar's dispatch + combine)
         ms_nl = self.run_without_layout(steps) if extra else None
         if ms_nl is not None:
@@ -371,6 +434,8 @@ class Runner:
                                      "frac_of_peak": round(b / (ms_nl * 1e-3) / 1e9
                                                            / PEAK_HBM_GBPS, 4)}
         res.update(self.extra)
+        if self.msgs is not None and extra:
+            res["execute_ms_by_publish_batch"] = self.publish_curve()
         if total < 256e6:
             res["cache"] = "warm: the step's data fits in the 256 MB last-level cache"
         if total < 256e6 and extra:
@@ -384,24 +449,71 @@ class Runner:
         return ms, res
 
 
-def copy_probe(torch, nbytes=4 << 30, reps=10):
-    """Device-to-device copy bandwidth (read + write bytes / time)."""
-    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
-    b = torch.empty_like(a)
-    a.fill_(1.0)
-    for _ in range(2):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    del a, b
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
+PROBE_KINDS = {"read": 0, "write": 1, "copy": 2}
+
+
+def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
+    """HBM read-only, write-only and copy rates of the hand-written probe
+    kernels (bench_probe.hip), each the best over vectors in flight per
+    thread (1, 2, 4, 8), plain or non-temporal accesses and three grid
+    sizes; bytes moved / mean event time of `reps` launches on 4 GiB
+    buffers.  These are the device's measured roofs for streams that only
+    read or only write, next to which the method's mix of reads and writes
+    is judged."""
+    import ctypes
+
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError(f"{PROBE_LIB} is not built; run combine_ep_get_layout_amd/build.py")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.bench_probe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.bench_probe_launch.restype = ctypes.c_int
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    a.fill_(7)
+    b.fill_(0)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, kind in PROBE_KINDS.items():
+        best = (0.0, None)
+        for unroll in (1, 2, 4, 8):
+            for nt in (0, 1):
+                for blocks in (2048, 8192, 32768):
+                    src, dst = (a, sink) if kind == 0 else (a, b)
+
+                    def launch():
+                        st = lib.bench_probe_launch(kind, src.data_ptr(), dst.data_ptr(), nbytes,
+                                                    unroll, nt, blocks, stream)
+                        if st != 0:
+                            raise RuntimeError("probe launch failed")
+
+                    launch()
+                    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s.record()
+                    for _ in range(reps):
+                        launch()
+                    e.record()
+                    torch.cuda.synchronize()
+                    moved = nbytes * (2 if kind == 2 else 1)
+                    rate = moved / (s.elapsed_time(e) / reps * 1e-3) / 1e9
+                    if rate > best[0]:
+                        best = (rate, {"unroll": unroll, "nt": nt, "blocks": blocks})
+        out[name + "_GBps"] = round(best[0], 1)
+        out[name + "_config"] = best[1]
+    del a, b, sink
     torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    out["source"] = "bench_probe.hip (16-byte vector streams, 4 GiB buffers)"
+    return out
+
+
+def mix_ceiling(rw, probes):
+    """Time (ms) at the probes' roofs for `rw` = (read, written) bytes when
+    reads and writes take turns: read / read rate + written / write rate."""
+    r, wr = rw
+    return (r / (probes["read_GBps"] * 1e9) + wr / (probes["write_GBps"] * 1e9)) * 1e3
 
 
 def cpu_baseline(w, host, tokens_per_rank, min_seconds):
@@ -484,6 +596,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the without-layout and cold-cache passes (profiler runs, so "
                          "every launch of a kernel is a warm launch of the timed step)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the bandwidth probes (and the mix-ceiling fractions)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain copy of 2^30 bytes (counter calibration)")
     args = ap.parse_args()
@@ -497,6 +611,10 @@ def main():
     from combine_ep_get_layout_amd import ep, inputs
 
     ep.lib()  # fail loudly if the HIP library is missing
+    probes = None
+    if not args.no_probes:
+        log("[bench] bandwidth probes")
+        probes = bandwidth_probes(torch)
     names = [n for n in args.workloads.split(",") if n]
     head = None
     others = {}
@@ -506,7 +624,7 @@ def main():
         fused = args.fused == "on" or (args.fused == "auto" and name in FUSED_WORKLOADS)
         r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu), fused=fused)
         steps = args.steps if i == 0 else max(5, min(args.steps, 50))
-        ms, res = r.report(steps, args.warmup, extra=not args.no_extra)
+        ms, res = r.report(steps, args.warmup, extra=not args.no_extra, probes=probes)
         if i == 0:
             head = (w, ms, res)
             if not args.no_cpu:
@@ -522,7 +640,6 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
-    probe = copy_probe(torch)
     w, ms, res = head
     if not args.no_cpu and w.mode != ep.MODE_MESSAGES:
         cpu = cpu_baseline(w, host, min(args.cpu_tokens or w.T, w.T), args.cpu_seconds)
@@ -548,8 +665,8 @@ def main():
         "phases": res["phases"],
         "roofline": res["roofline"],
         "without_layout": res.get("without_layout"),
-        "copy_probe_GBps": round(probe, 1),
-        "frac_of_copy_probe": round(res["GBps"] / probe, 4),
+        "mix_ceiling": res.get("mix_ceiling"),
+        "bandwidth_probes": probes,
         "workloads": others,
         "cpu_baseline": cpu,
     }

@@ -53,6 +53,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The bench's bandwidth probes (bench_probe.hip, beside bench.py) as
+    their own library, libbench_probe.so; they are not part of libep."""
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)

@@ -35,6 +35,26 @@ __device__ __forceinline__ uint64_t first_rows(int myrow, int K) {
   return __ballot(lane_id() < K && myrow >= 0 && !dup);
 }
 
+// Entries whose row is not read (masked, rank-major repeats, rows past y)
+// still issue loads, of a stand-in row: the token's first row that is read
+// anyway, whose lines the same wavefront fetches, so the stand-in costs no
+// HBM bytes.  The loads stay unconditional because a branch around a load
+// makes the compiler wait for every load issued before it, which would
+// serialise a group's loads (measured on MI355X: the two-token pipeline at
+// hidden 4096 was 18% slower with branches).  -1: the token reads no row.
+__device__ __forceinline__ int stand_in_row(int myrow, uint64_t keep, int K, int64_t y_rows) {
+  const int lane = lane_id();
+  const uint64_t ok = __ballot(lane < K && myrow >= 0 && myrow < y_rows && ((keep >> lane) & 1));
+  return ok ? __builtin_amdgcn_readlane(myrow, __builtin_ctzll(ok)) : -1;
+}
+
+// Row whose loads entry k issues: its own when it is read, else the stand-in.
+__device__ __forceinline__ int read_row(int myrow, uint64_t keep, int k, int K, int64_t y_rows,
+                                        int stand_in) {
+  const int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
+  return row >= 0 && row < y_rows && ((keep >> k) & 1) ? row : stand_in;
+}
+
 // RM (rank-major): sum the token's distinct rows with weight 1 and skip the
 // loads of repeated rows.  SERIAL: one row's loads (NV vectors per lane) in
 // flight per wavefront, each row waiting for the previous one.
@@ -50,30 +70,42 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
   const int myrow = lane < K ? send_pos[(int64_t)tok * K + lane] : -1;
   const float myw = RM ? 1.0f : (lane < K ? w[(int64_t)tok * K + lane] : 0.0f);
   const uint64_t keep = RM ? first_rows(myrow, K) : ~0ull;
+  // nothing branches on the loaded rows before the loop (only y_rows, a
+  // launch argument), so the loop's setup overlaps the index loads; a token
+  // that reads no row at all loads row 0's lines as its stand-in
+  const int stand_in = max(stand_in_row(myrow, keep, K, y_rows), 0);
   constexpr int kGroup = SERIAL ? 1 : (NV == 1 ? 8 : (NV == 2 ? 4 : 2));
   float acc[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += kGroup) {
+  for (int k0 = 0; y_rows > 0 && k0 < K; k0 += kGroup) {
     u32x4 v[kGroup][NV];
 #pragma unroll
     for (int kk = 0; kk < kGroup; ++kk) {
       const int k = k0 + kk;
-      int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
-      if (RM && !((keep >> k) & 1)) row = -1;
-      if (row >= y_rows) {
-        if (lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
-        row = -1;
+      if (RM) {
+        // rank-major: a repeated row (about three of a token's eight at the
+        // prefill routing) is not read at all; a stand-in load per repeat
+        // made this combine 15% slower on MI355X
+        const int row = read_row(myrow, keep, k, K, y_rows, -1);
+        const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          if (row < 0) {
+            v[kk][i] = u32x4{0u, 0u, 0u, 0u};
+            continue;
+          }
+          v[kk][i] = __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1));
+        }
+        continue;
       }
-      // masked entries, rank-major repeats and rows past y are not read
-      // (row is uniform across the wavefront: no divergence)
-      const u32x4* src = y + (int64_t)(row < 0 ? 0 : row) * V;
+      const int row = read_row(myrow, keep, k, K, y_rows, stand_in);
+      const u32x4* src = y + (int64_t)row * V;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        v[kk][i] = row >= 0 ? __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1))
-                            : u32x4{0u, 0u, 0u, 0u};
+        v[kk][i] = __builtin_nontemporal_load(src + min(base + lane + kWave * i, V - 1));
     }
 #pragma unroll
     for (int kk = 0; kk < kGroup; ++kk) {
@@ -92,6 +124,8 @@ __global__ __launch_bounds__(1024) void combine_rows(const u32x4* __restrict__ y
         }
     }
   }
+  const bool past = __ballot(lane < K && myrow >= y_rows) != 0;  // every lane takes part
+  if (past && lane == 0 && base == 0) set_err(err, EP_DEVERR_CAPACITY);
   u32x4* dst = out + (int64_t)tok * V;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -113,19 +147,28 @@ constexpr int kPipeK = 8;
 constexpr int kPipeTokens = 2;
 constexpr int64_t kPipeMinTokens = 8192;
 
-// Loads of one token's (up to kPipeK) rows, one vector per lane.  Rows the
-// mask drops (masked entries, rank-major repeats, rows past y) are not read.
+// Loads of one token's (up to kPipeK) rows, one vector per lane; entries
+// whose row is not read load the stand-in row (a token that reads no row
+// at all loads row 0's lines, its only HBM cost), so the previous token's
+// loads stay in flight meanwhile.
 template <bool RM>
 __device__ __forceinline__ void load_rows8(const u32x4* __restrict__ y, int myrow, uint64_t keep,
                                            int K, int j, int V, int64_t y_rows,
                                            u32x4 (&v)[kPipeK]) {
+  if (y_rows == 0) {  // nothing to read; every entry is skipped (uniform per launch)
+#pragma unroll
+    for (int k = 0; k < kPipeK; ++k) v[k] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int stand_in = RM ? -1 : max(stand_in_row(myrow, keep, K, y_rows), 0);
 #pragma unroll
   for (int k = 0; k < kPipeK; ++k) {
-    int row = k < K ? __builtin_amdgcn_readlane(myrow, k) : -1;
-    if (RM && !((keep >> k) & 1)) row = -1;
-    if (row >= y_rows) row = -1;
-    v[k] = row >= 0 ? __builtin_nontemporal_load(y + (int64_t)row * V + min(j, V - 1))
-                    : u32x4{0u, 0u, 0u, 0u};
+    const int row = read_row(myrow, keep, k, K, y_rows, stand_in);
+    if (RM && row < 0) {  // rank-major repeats are not read (as in combine_rows)
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
+    v[k] = __builtin_nontemporal_load(y + (int64_t)row * V + min(j, V - 1));
   }
 }
 

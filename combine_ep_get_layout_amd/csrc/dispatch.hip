@@ -269,7 +269,8 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
                                                      u32x4* __restrict__ codes,
                                                      void* __restrict__ scales, int P, int K,
                                                      int64_t cap, int G, int RT, int n_tok,
-                                                     int32_t* err, RowMeta meta, LayoutArgs la) {
+                                                     int32_t* err, RowMeta meta, LayoutArgs la,
+                                                     bool tok_stage) {
   const int lane = threadIdx.x & 63;
   __shared__ int start[FU && !LL ? 2049 : 1];
   if (FU) {
@@ -307,6 +308,21 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
   const bool meta_wave = RM && base == 0 && (meta.idx || meta.wts);
   const int myid = meta_wave && lane < K ? meta.topk[(int64_t)tok * K + lane] : -1;
   const float myw = meta_wave && meta.wts && lane < K ? meta.w[(int64_t)tok * K + lane] : 0.0f;
+  // with the row -> token map: the token's G scales go to the staging once
+  // ([token][G], consecutive tokens in consecutive bytes); a second kernel
+  // places them in every row's column entries
+  const bool row_scales = !tok_stage;
+  if (!row_scales) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int j = base + lane + kWave * i;
+      if (j < P && (lane & 7) == 0) {
+        const int64_t si = (int64_t)tok * G + (j >> 3);
+        if (Q == EP_QUANT_FP8_F32) ((float*)scales)[si] = scf[i];
+        else ((uint8_t*)scales)[si] = (uint8_t)sce[i];
+      }
+    }
+  }
   for (int k = 0; k < K; ++k) {
     if (RM && !((keep >> k) & 1)) continue;
     const int row = __builtin_amdgcn_readlane(myrow, k);
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(NP >= 3 ? 512 : 1024) void dispatch_fp8(const u32x4
       const int j = base + lane + kWave * i;
       if (j < P) {
         dst[j] = cv[i];
-        if ((lane & 7) == 0) {
+        if (row_scales && (lane & 7) == 0) {
           const int64_t si = sbase + (int64_t)(j >> 3) * sstride;
           if (Q == EP_QUANT_FP8_F32)
             ((float*)scales)[si] = scf[i];
@@ -409,6 +425,126 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
   }
 }
 
+// Normal-mode and rank-major FP8 scales from the per-token staging: the
+// dispatch kernel stored each token's G scales once, at stage[tok * G]; a
+// block takes tile_rows consecutive receive rows, reads each row's token
+// from the layout's recv_src_idx (-1: alignment padding, never written),
+// gathers the tokens' scale rows into LDS and writes the tile's part of
+// every column scales[g * cap + row] as 16-byte vectors (16 / SB rows of one
+// group each), entry by entry where a vector would cover a padding row or
+// run past the filled rows, or where the columns are not 16-byte aligned
+// (vec_ok = 0).  Against one staged copy per receive row, the staging
+// shrinks K-fold and is written by consecutive tokens into whole lines.
+template <int SB>
+__global__ __launch_bounds__(256) void scales_from_tokens(const uint8_t* __restrict__ stage,
+                                                          uint8_t* __restrict__ scales, int G,
+                                                          int64_t cap, int64_t limit,
+                                                          const int32_t* row_base_end,
+                                                          const int32_t* __restrict__ row_token,
+                                                          int n_tok, int tile_rows, int vec_ok) {
+  extern __shared__ uint32_t lds[];
+  int* tok = (int*)lds;                                // tile_rows
+  uint8_t* tile = (uint8_t*)(lds + tile_rows);         // tile_rows * G * SB bytes
+  const int64_t total = min((int64_t)*row_base_end, limit);
+  const int64_t r0 = (int64_t)blockIdx.x * tile_rows;
+  if (r0 >= total) return;
+  const int nrows = (int)min((int64_t)tile_rows, total - r0);
+  // a token index outside [0, n_tok) counts as padding: nothing is read for it
+  for (int r = threadIdx.x; r < tile_rows; r += blockDim.x) {
+    const int t = r < nrows ? row_token[r0 + r] : -1;
+    tok[r] = t < n_tok ? t : -1;
+  }
+  __syncthreads();
+  const int rb = G * SB;  // bytes of one token's scales
+  if (rb % 4 == 0) {
+    const int nw = rb / 4;
+    for (int i = threadIdx.x; i < nrows * nw; i += blockDim.x) {
+      const int r = i / nw, q = i - r * nw;
+      const int t = tok[r];
+      ((uint32_t*)tile)[i] = t >= 0 ? ((const uint32_t*)stage)[(int64_t)t * nw + q] : 0u;
+    }
+  } else {
+    for (int i = threadIdx.x; i < nrows * rb; i += blockDim.x) {
+      const int r = i / rb, q = i - r * rb;
+      const int t = tok[r];
+      tile[i] = t >= 0 ? stage[(int64_t)t * rb + q] : (uint8_t)0;
+    }
+  }
+  __syncthreads();
+  constexpr int kPer = 16 / SB;  // rows per column vector
+  const int nvec = tile_rows / kPer;
+  // consecutive threads take consecutive groups of the same rows, so their
+  // LDS reads fall in the same few words
+  for (int it = threadIdx.x; it < G * nvec; it += blockDim.x) {
+    const int g = it % G, rv = (it / G) * kPer;
+    bool full = vec_ok && rv + kPer <= nrows;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) full = full && tok[rv + q] >= 0;
+    const int64_t di = (int64_t)g * cap + r0 + rv;
+    if (full) {
+      u32x4 v;
+      if (SB == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ((const uint32_t*)tile)[(rv + q) * G + g];
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) word |= (uint32_t)tile[(rv + 4 * w + b) * rb + g] << (8 * b);
+          v[w] = word;
+        }
+      }
+      *(u32x4*)(scales + di * SB) = v;
+    } else {
+      for (int q = 0; q < kPer; ++q) {
+        const int r = rv + q;
+        if (r >= nrows || tok[r] < 0) continue;
+        if (SB == 4) ((uint32_t*)scales)[di + q] = ((const uint32_t*)tile)[r * G + g];
+        else scales[di + q] = tile[r * rb + g];
+      }
+    }
+  }
+}
+
+// Low-latency FP8 scales from the per-token staging ("DeepEP" deep dive,
+// sec. 1.2: column-major scales per expert, [E][G][R*T]): block (e, tile)
+// takes the expert's slots [tile * kLLTile, ...) below its receive count,
+// reads each slot's token from recv_src_idx and writes the tile's part of
+// every column (e, g), consecutive threads on consecutive slots.  The ~32
+// slots an expert receives at the decode shape then fill their 128-byte
+// column line from one block, instead of 4 bytes at a time from 32 token
+// blocks on several dies.  Slots past the count are not written.
+constexpr int kLLTile = 256;
+
+template <int SB>
+__global__ __launch_bounds__(256) void scales_ll_from_tokens(const uint8_t* __restrict__ stage,
+                                                             uint8_t* __restrict__ scales, int G,
+                                                             int rt,
+                                                             const int32_t* __restrict__ count,
+                                                             const int32_t* __restrict__ row_token,
+                                                             int n_tok) {
+  __shared__ int tok[kLLTile];
+  const int e = blockIdx.x;
+  const int p0 = blockIdx.y * kLLTile;
+  const int n = min(count[e], rt);  // positions past R*T were refused by the layout
+  if (p0 >= n) return;
+  const int np = min(kLLTile, n - p0);
+  for (int q = threadIdx.x; q < np; q += blockDim.x) {
+    const int t = row_token[(int64_t)e * rt + p0 + q];
+    tok[q] = t >= 0 && t < n_tok ? t : -1;  // a token index out of range reads nothing
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < G * np; it += blockDim.x) {
+    const int g = it / np, q = it - g * np;
+    const int t = tok[q];
+    if (t < 0) continue;
+    const int64_t di = ((int64_t)e * G + g) * rt + p0 + q;
+    if (SB == 4) ((uint32_t*)scales)[di] = ((const uint32_t*)stage)[(int64_t)t * G + g];
+    else scales[di] = stage[(int64_t)t * G + g];
+  }
+}
+
 inline RowMeta row_meta(const DispatchArgs& a) {
   RowMeta m;
   m.topk = a.topk;
@@ -467,22 +603,49 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
   // stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
   const int blocks = LL ? xcd_blocks(N) : N;
+  const bool tok_stage = a.row_token != nullptr;
+  void* sc = LL && !tok_stage ? a.recv_scales : a.stage;
   if (a.fused && !RM)
     hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, false, true>), dim3(fused_blocks(a, blocks)),
                        dim3(kWave * waves), 0, st, (const u32x4*)a.x, a.send_pos,
-                       (u32x4*)a.recv_x, LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G,
-                       a.g.R * a.g.T, N, a.err, row_meta(a), a.la);
+                       (u32x4*)a.recv_x, sc, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N, a.err,
+                       row_meta(a), a.la, tok_stage);
   else
     hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, RM, false>), dim3(blocks), dim3(kWave * waves),
-                       0, st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x,
-                       LL ? a.recv_scales : a.stage, P, a.g.K, cap, a.g.G, a.g.R * a.g.T, N,
-                       a.err, row_meta(a), a.la);
+                       0, st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, sc, P, a.g.K,
+                       cap, a.g.G, a.g.R * a.g.T, N, a.err, row_meta(a), a.la, tok_stage);
+  if (LL && tok_stage) {
+    const int rt = a.g.R * a.g.T;
+    const dim3 grid((unsigned)a.g.E, (unsigned)((rt + kLLTile - 1) / kLLTile));
+    if (Q == EP_QUANT_FP8_F32)
+      hipLaunchKernelGGL(scales_ll_from_tokens<4>, grid, dim3(256), 0, st, (const uint8_t*)a.stage,
+                         (uint8_t*)a.recv_scales, a.g.G, rt, a.recv_per_expert, a.row_token, N);
+    else
+      hipLaunchKernelGGL(scales_ll_from_tokens<1>, grid, dim3(256), 0, st, (const uint8_t*)a.stage,
+                         (uint8_t*)a.recv_scales, a.g.G, rt, a.recv_per_expert, a.row_token, N);
+  }
   if (!LL) {
     // 256 rows per tile, fewer for wide rows (the tile lives in LDS), at
     // least 16 (16-byte aligned tiles)
     const int sb = Q == EP_QUANT_FP8_F32 ? 4 : 1;
     int tile_rows = 256;
     while (tile_rows > 16 && (size_t)tile_rows * a.g.G * sb > 32768) tile_rows >>= 1;
+    if (tok_stage) {
+      const size_t lds = sizeof(int) * (size_t)tile_rows + (size_t)tile_rows * a.g.G * sb;
+      const int vec_ok = ((a.cap * sb) % 16 == 0 && ((uintptr_t)a.recv_scales % 16) == 0) ? 1 : 0;
+      const int64_t tiles = (cap + tile_rows - 1) / tile_rows;
+      if (tiles > 0) {
+        if (Q == EP_QUANT_FP8_F32)
+          hipLaunchKernelGGL(scales_from_tokens<4>, dim3((unsigned)tiles), dim3(256), lds, st,
+                             (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
+                             a.row_base + a.g.R, a.row_token, N, tile_rows, vec_ok);
+        else
+          hipLaunchKernelGGL(scales_from_tokens<1>, dim3((unsigned)tiles), dim3(256), lds, st,
+                             (const uint8_t*)a.stage, (uint8_t*)a.recv_scales, a.g.G, a.cap, cap,
+                             a.row_base + a.g.R, a.row_token, N, tile_rows, vec_ok);
+      }
+      return;
+    }
     const size_t lds = sizeof(int) * ((a.g.E + 1 + tile_rows + 3) & ~3) +
                        (size_t)tile_rows * a.g.G * sb;
     const int all_filled = RM || a.align == 1 ? 1 : 0;

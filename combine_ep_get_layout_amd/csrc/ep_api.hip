@@ -110,6 +110,10 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
                              : entries + (int64_t)E * (p->expert_alignment - 1);
     off += up256((size_t)rows * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
   }
+#ifdef EP_LL_TOKEN_SCALES
+  if (p->mode == EP_MODE_LOW_LATENCY && p->quant != EP_QUANT_NONE)  // one row per token
+    off += up256((size_t)R * T * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
+#endif
   g->ws_bytes = off < 256 ? 256 : off;
   return EP_OK;
 }
@@ -302,8 +306,17 @@ int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layou
   if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
     return EP_ERR_CAPACITY;
   const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;
+  const int64_t ll_rows = (int64_t)g.E * g.R * g.T;
+#ifdef EP_LL_TOKEN_SCALES
+  // low-latency FP8 with the layout's row -> token map: scales staged per
+  // token, then gathered into the column-major per-expert array
+  const bool ll_tok = p->mode == EP_MODE_LOW_LATENCY && p->quant != EP_QUANT_NONE &&
+                      layout->recv_src_idx && layout->recv_capacity >= ll_rows;
+#else
+  const bool ll_tok = false;
+#endif
   const bool staged =
-      (p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE;
+      ((p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE) || ll_tok;
   if (rank_major && toks) {
     // per-row metadata needs the routing (ids) and, for weights, the weights
     if ((recv->topk_idx || recv->topk_weights) && !topk_idx) return EP_ERR_NULL;
@@ -326,6 +339,12 @@ int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layou
   a->stage = staged ? (char*)workspace + g.off_stage : nullptr;
   a->stage_rows = rank_major ? (int64_t)g.R * g.T * (g.K < g.R ? g.K : g.R)
                             : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
+  // scales staged once per token when the layout's row -> token map covers
+  // every receive row (the staging holds stage_rows >= R*T rows either way)
+  const int64_t map_rows = p->mode == EP_MODE_LOW_LATENCY ? ll_rows : recv->capacity;
+  a->row_token = staged && layout->recv_src_idx && layout->recv_capacity >= map_rows
+                     ? layout->recv_src_idx
+                     : nullptr;
   a->align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;
   a->rank_major = rank_major;
   a->topk = rank_major ? topk_idx : nullptr;
@@ -444,7 +463,8 @@ int ep_dispatch_fused(const ep_problem* p, const int32_t* topk_idx, const ep_lay
 }
 
 int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv_arena,
-                        int64_t recv_capacity, int32_t* err, void* stream) {
+                        int64_t recv_capacity, int32_t publish_batch, int32_t* err,
+                        void* stream) {
   Geometry g;
   int st = ep::make_geometry(p, &g);
   if (st != EP_OK) return st;
@@ -458,8 +478,10 @@ int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv
       !aligned(err, 4))
     return EP_ERR_ALIGN;
   if (m->send_capacity < 0 || m->desc_capacity < 0 || recv_capacity < 0) return EP_ERR_CAPACITY;
-  if (m->desc_capacity > 0x7fffffff) return EP_ERR_SHAPE;  // one block per descriptor piece
+  if (m->desc_capacity > 0x7fffffff) return EP_ERR_SHAPE;  // descriptor indices are 31-bit
+  if (publish_batch < 0) return EP_ERR_SHAPE;
   ep::ExecArgs a;
+  a.publish_batch = publish_batch;
   a.g = g;
   a.region_bytes = p->region_bytes;
   a.send = m->send_arena;
@@ -479,11 +501,12 @@ int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv
 int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t* recv_arena,
                        int64_t recv_capacity, const int32_t* num_tokens_per_expert,
                        const ep_recv* out, int32_t* recv_count, int32_t* recv_src_idx,
-                       int32_t* err, void* stream) {
+                       int32_t spin_limit, int32_t* err, void* stream) {
   Geometry g;
   int st = ep::make_geometry(p, &g);
   if (st != EP_OK) return st;
   if (p->mode != EP_MODE_MESSAGES) return EP_ERR_MODE;
+  if (spin_limit < 0 || spin_limit > EP_MAX_SPIN) return EP_ERR_SHAPE;
   const int64_t rows = (int64_t)g.E * g.R * g.T;
   if (!m || !m->table || !out || !err || !recv_count || !num_tokens_per_expert)
     return EP_ERR_NULL;
@@ -508,6 +531,7 @@ int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t*
   a.recv_scales = out->scales;
   a.recv_count = recv_count;
   a.recv_src_idx = recv_src_idx;
+  a.spin_limit = spin_limit;
   a.err = err;
   if (ep::launch_unpack(a, (hipStream_t)stream) != hipSuccess) return EP_ERR_HIP;
   return EP_OK;

@@ -71,6 +71,10 @@ struct DispatchArgs {
   // segment starts / counts / row bases used to transpose it column-major
   void* stage;
   int64_t stage_rows;  // rows the staging buffer holds
+  // the layout's recv_src_idx when it covers every receive row: the
+  // staging then holds each token's scales once ([N][G]) and the transpose
+  // gathers them per row; NULL: one staged copy per receive row
+  const int32_t* row_token;
   int align;           // expert_alignment (normal mode; 1 otherwise)
   const int32_t* expert_start;
   const int32_t* recv_per_expert;
@@ -140,6 +144,7 @@ struct ExecArgs {
   const int64_t* num_desc;
   uint8_t* recv;             // receive arenas
   int64_t recv_cap;
+  int publish_batch;         // 0: flags in a second launch; B >= 1: every B messages
   int32_t* err;
 };
 
@@ -159,6 +164,7 @@ struct UnpackArgs {
   void* recv_scales;           // [E][G][R*T]
   int32_t* recv_count;         // [E]
   int32_t* recv_src_idx;       // [E*R*T]
+  int spin_limit;              // extra polls of a message's flag before giving up
   int32_t* err;
 };
 

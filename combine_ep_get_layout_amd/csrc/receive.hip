@@ -12,15 +12,19 @@
 // per expert, recv_count); sec. 2.1: the per-expert counts ranks exchange
 // before the data, which give every source's first slot.
 //
-// Execute, two launches:
+// Execute, publication batch 0, two launches:
 //   1. every descriptor except the last one of each message (its flag), cut
 //      into pieces of at most kPieceBytes; one block per (descriptor, piece)
 //      copies with 16-byte vectors through LDS, 64 KiB per round;
 //   2. one thread per message copies its flag.
 //   The launch boundary puts every payload and header before every flag.
+// Execute, publication batch B >= 1, one launch: each workgroup copies a
+// run of messages and announces their flags B messages at a time, each
+// batch behind a release fence (msg_exec_batched).
 // Unpack, one launch: one block of eight wavefronts per (source,
-// destination) message.  Thread 0 checks the header and the flag once (no
-// waiting: a message that fails is reported and skipped).  The message's
+// destination) message.  Thread 0 polls the message's flag with acquire
+// loads, at most 1 + spin_limit times, then checks the header and the flag
+// (a message that fails is reported and skipped).  The message's
 // entries are taken in segments: the wavefronts first rank the segment's
 // expert ids, one local expert each, with one ballot per 64 entries (each
 // match takes the next slot of its expert after the slots of earlier
@@ -155,6 +159,72 @@ __global__ __launch_bounds__(256) void msg_exec_flags(ExecArgs a) {
   for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
 }
 
+// Batched publication (publish_batch = B >= 1), one launch ("GPU-Initiated
+// Communication: Dissecting Down to the Bone", Doorbell Batching: one
+// notification for a batch of work requests; Sharing a QP: slots reserved,
+// filled in parallel, announced in reservation order; "ibgda_device.cuh"
+// notes, sec. 4: a doorbell after every few requests).  Workgroup w takes
+// the table entries [w * per, (w + 1) * per) in reservation order -- the
+// (source, destination) order in which the packer numbered the descriptors
+// -- and copies each message's payload and header pieces with all its
+// threads.  After every B messages of its run, and after the last, it
+// publishes that batch: every thread releases its copies (device-scope
+// fence), a workgroup barrier, then the batch's flags, one thread each.  A
+// workgroup's batches are thus announced in order, each after its own data;
+// no workgroup waits for another.
+__device__ inline void publish_flags(const ExecArgs& a, int64_t m_lo, int64_t m_hi,
+                                     int64_t live) {
+  __threadfence();  // this thread's payload and header stores, device-wide
+  __syncthreads();  // ... and every other thread's, before any flag
+  for (int64_t m = m_lo + threadIdx.x; m < m_hi; m += blockDim.x) {
+    const int64_t* row = a.table + m * 8;
+    if (row[3] <= 0 || row[6] <= 0) continue;
+    const int64_t i = row[5] + row[6] - 1;
+    if (i >= live) continue;
+    Put p;
+    const int bad = read_put(a, i, &p);
+    if (bad) {
+      set_err(a.err, bad);
+      continue;
+    }
+    if (p.len == 16 && ((p.src | p.dst) & 15) == 0) {
+      *(u32x4*)(a.recv + p.dst) = *(const u32x4*)(a.send + p.src);
+    } else {
+      for (int64_t o = 0; o < p.len; ++o) a.recv[p.dst + o] = a.send[p.src + o];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kExecThreads) void msg_exec_batched(ExecArgs a, int64_t per) {
+  const int64_t rr = (int64_t)a.g.R * a.g.R;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < rr ? lo + per : rr;
+  const int64_t live = live_descriptors(a);
+  int64_t batch_lo = lo;
+  int in_batch = 0;
+  for (int64_t m = lo; m < hi; ++m) {  // uniform across the block
+    const int64_t* row = a.table + m * 8;
+    if (row[3] > 0 && row[6] > 0) {
+      const int64_t first = row[5], flag = row[5] + row[6] - 1;
+      for (int64_t i = first; i < flag && i < live; ++i) {
+        Put p;
+        const int bad = read_put(a, i, &p);
+        if (bad) {
+          if (threadIdx.x == 0) set_err(a.err, bad);
+          continue;
+        }
+        copy_range(a, p, 0, p.len);
+      }
+      ++in_batch;
+    }
+    if (in_batch == a.publish_batch || (m == hi - 1 && in_batch > 0)) {
+      publish_flags(a, batch_lo, m + 1, live);
+      batch_lo = m + 1;
+      in_batch = 0;
+    }
+  }
+}
+
 // Unpack: one block per (s, d), ranking and copying as described at the
 // top of this file.  Die-aware order: workgroups are dealt to the chip's
 // kXcds dies round-robin, so block b runs on die b % kXcds.  Destination d
@@ -224,12 +294,24 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   const uint8_t* msg = a.arena + off;
   __shared__ int ok;
   if (threadIdx.x == 0) {
-    const u32x4 hd = *(const u32x4*)msg;
-    int good = hd[0] == (uint32_t)s && hd[1] == (uint32_t)d && hd[2] == (uint32_t)n &&
-               hd[3] == (uint32_t)body && body == ms.body && reg == 32 + body;
+    // the table's sizes first: they place the flag inside the region
+    int good = body == ms.body && reg == 32 + body;
+    if (good && a.spin_limit > 0) {
+      // poll the flag's first word with acquire loads (the stores it
+      // announces become visible with it) until it shows the epoch, at most
+      // spin_limit times, sleeping between polls; then check as below
+      uint32_t* f0 = (uint32_t*)(uintptr_t)(msg + 16 + body);
+      for (int it = 0; it < a.spin_limit &&
+                       __hip_atomic_load(f0, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != a.epoch;
+           ++it)
+        __builtin_amdgcn_s_sleep(8);
+    }
     if (good) {
+      const u32x4 hd = *(const u32x4*)msg;
       const u32x4 fl = *(const u32x4*)(msg + 16 + body);
-      good = fl[0] == a.epoch && fl[1] == 0u && fl[2] == 0u && fl[3] == 0u;
+      good = hd[0] == (uint32_t)s && hd[1] == (uint32_t)d && hd[2] == (uint32_t)n &&
+             hd[3] == (uint32_t)body && fl[0] == a.epoch && fl[1] == 0u && fl[2] == 0u &&
+             fl[3] == 0u;
     }
     if (!good) set_err(a.err, EP_DEVERR_MESSAGE);
     ok = good;
@@ -331,8 +413,19 @@ __global__ __launch_bounds__(1024) void msg_unpack(UnpackArgs a) {
   }
 }
 
+// Workgroups of the batched form: two 1024-thread groups per compute unit.
+constexpr int64_t kBatchedGroups = 512;
+
 hipError_t launch_execute(const ExecArgs& a, hipStream_t st) {
   const int R = a.g.R;
+  if (a.publish_batch > 0) {
+    const int64_t rr = (int64_t)R * R;
+    const int64_t per = (rr + kBatchedGroups - 1) / kBatchedGroups;
+    const int64_t groups = (rr + per - 1) / per;
+    hipLaunchKernelGGL(msg_exec_batched, dim3((unsigned)groups), dim3(kExecThreads), 0, st, a,
+                       per);
+    return hipGetLastError();
+  }
   // pieces of at least kPieceBytes, at most kMaxPieces per descriptor (a
   // descriptor never exceeds region_bytes)
   int64_t piece = kPieceBytes;

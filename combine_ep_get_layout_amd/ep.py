@@ -97,11 +97,12 @@ def lib() -> ctypes.CDLL:
         l.ep_dispatch_fused_noalloc.restype = ctypes.c_int
         l.ep_combine.argtypes = [P, ctypes.POINTER(CLayout), _vp, ctypes.c_int64, _vp, _vp, _vp]
         l.ep_combine.restype = ctypes.c_int
-        l.ep_messages_execute.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64, _vp,
-                                          _vp]
+        l.ep_messages_execute.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64,
+                                          ctypes.c_int32, _vp, _vp]
         l.ep_messages_execute.restype = ctypes.c_int
         l.ep_messages_unpack.argtypes = [P, ctypes.POINTER(CMessages), _vp, ctypes.c_int64, _vp,
-                                         ctypes.POINTER(CRecv), _vp, _vp, _vp, _vp]
+                                         ctypes.POINTER(CRecv), _vp, _vp, ctypes.c_int32, _vp,
+                                         _vp]
         l.ep_messages_unpack.restype = ctypes.c_int
         l.ep_status_string.argtypes = [ctypes.c_int]
         l.ep_status_string.restype = ctypes.c_char_p
@@ -132,6 +133,45 @@ def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+class _Args:
+    """A libep entry point's name, its C arguments except the stream, and
+    the ctypes objects those arguments point into (kept alive with them)."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple = ()):
+        self.name, self.args, self.keep = name, args, keep
+
+
+def _invoke(a: _Args, stream) -> None:
+    _check(getattr(lib(), a.name)(*a.args, _stream(stream)), a.name)
+
+
+class Call:
+    """One libep call whose arguments were checked and marshalled once, when
+    it was made (ep.prepare): calling it hands the cached C structs, device
+    pointers and stream handle to the library and nothing else.  The
+    tensors it was made from must stay alive and unchanged in size; their
+    contents may change between calls."""
+
+    def __init__(self, a: _Args, stream=None):
+        self.name = a.name
+        self._fn = getattr(lib(), a.name)
+        self._args = a.args + (_stream(stream),)
+        self._keep = a.keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise EPError(st, self.name)
+
+
+def prepare(fn, *args, stream=None, **kw) -> Call:
+    """ep.prepare(ep.dispatch, p, layout, x, recv=..., ws=...) checks the
+    arguments as fn would and returns a Call that repeats the call with
+    them on `stream` (torch's current stream when it was prepared by
+    default)."""
+    return Call(_ARGS[fn](*args, **kw), stream)
 
 
 @dataclass
@@ -217,6 +257,11 @@ def _need(cond: bool, what: str):
 
 def get_layout(p: Problem, topk_idx: torch.Tensor, layout: Layout, ws: torch.Tensor,
                stream=None) -> None:
+    _invoke(_get_layout_args(p, topk_idx, layout, ws), stream)
+
+
+def _get_layout_args(p: Problem, topk_idx: torch.Tensor, layout: Layout,
+                     ws: torch.Tensor) -> _Args:
     R, T, E, K = p.R, p.T, p.E, p.K
     _need(topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32")
     _need(layout.num_tokens_per_expert.numel() == R * E and layout.is_token_in_rank.numel() == R * T * R,
@@ -226,9 +271,9 @@ def get_layout(p: Problem, topk_idx: torch.Tensor, layout: Layout, ws: torch.Ten
     _need(layout.recv_src_idx is None or layout.recv_src_idx.numel() >= layout.recv_capacity,
           "recv_src_idx smaller than recv_capacity")
     _need(ws.numel() >= workspace_bytes(p), "workspace too small")
-    cl = layout.c()
-    _check(lib().ep_get_layout(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl), _ptr(ws),
-                               ws.numel(), _stream(stream)), "ep_get_layout")
+    pc, cl = p.c(), layout.c()
+    return _Args("ep_get_layout", (ctypes.byref(pc), _ptr(topk_idx), ctypes.byref(cl), _ptr(ws),
+                                   ws.numel()), (pc, cl))
 
 
 class Recv:
@@ -282,6 +327,14 @@ def dispatch(p: Problem, layout: Layout, x: torch.Tensor, *, recv: Recv | None =
              msgs: Messages | None = None, topk_idx: torch.Tensor | None = None,
              topk_weights: torch.Tensor | None = None, ws: torch.Tensor | None = None,
              stream=None) -> None:
+    _invoke(_dispatch_args(p, layout, x, recv=recv, msgs=msgs, topk_idx=topk_idx,
+                           topk_weights=topk_weights, ws=ws), stream)
+
+
+def _dispatch_args(p: Problem, layout: Layout, x: torch.Tensor, *, recv: Recv | None = None,
+                   msgs: Messages | None = None, topk_idx: torch.Tensor | None = None,
+                   topk_weights: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None) -> _Args:
     R, T, H, E, K = p.R, p.T, p.H, p.E, p.K
     _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
     if p.mode != MODE_MESSAGES:
@@ -310,20 +363,24 @@ def dispatch(p: Problem, layout: Layout, x: torch.Tensor, *, recv: Recv | None =
         _need(msgs.send_arena.numel() >= msgs.send_capacity, "send arena")
         _need(msgs.descriptors.shape[0] >= msgs.desc_capacity, "descriptors")
         _need(ws is not None and ws.numel() >= workspace_bytes(p), "workspace too small")
-    cl = layout.c()
+    pc, cl = p.c(), layout.c()
     cr = recv.c() if recv is not None else None
     cm = msgs.c() if msgs is not None else None
-    _check(lib().ep_dispatch(ctypes.byref(p.c()), ctypes.byref(cl), _ptr(x), _ptr(topk_idx),
-                             _ptr(topk_weights), ctypes.byref(cr) if cr is not None else None,
-                             ctypes.byref(cm) if cm is not None else None, _ptr(ws),
-                             ws.numel() if ws is not None else 0, _stream(stream)),
-           "ep_dispatch")
+    return _Args("ep_dispatch", (ctypes.byref(pc), ctypes.byref(cl), _ptr(x), _ptr(topk_idx),
+                                 _ptr(topk_weights), ctypes.byref(cr) if cr is not None else None,
+                                 ctypes.byref(cm) if cm is not None else None, _ptr(ws),
+                                 ws.numel() if ws is not None else 0), (pc, cl, cr, cm))
 
 
 def dispatch_fused(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
                    recv: Recv, ws: torch.Tensor, stream=None) -> None:
     """Layout and dispatch in one call (normal / low-latency modes): fills
     `layout` exactly as get_layout does and `recv` as dispatch does."""
+    _invoke(_dispatch_fused_args(p, topk_idx, layout, x, recv, ws), stream)
+
+
+def _check_fused(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
+                 recv: Recv) -> None:
     R, T, H, E, K = p.R, p.T, p.H, p.E, p.K
     _need(p.mode in (MODE_NORMAL, MODE_LOW_LATENCY), "normal or low-latency problem")
     _need(topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32")
@@ -333,7 +390,6 @@ def dispatch_fused(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.
     _need(layout.send_head is None or layout.send_head.numel() == R * T * R, "send_head [R][T][R]")
     _need(layout.recv_src_idx is None or layout.recv_src_idx.numel() >= layout.recv_capacity,
           "recv_src_idx smaller than recv_capacity")
-    _need(ws.numel() >= workspace_bytes(p), "workspace too small")
     _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
     _need(recv.x.shape[0] >= recv.capacity and recv.x.shape[1] == H, "recv x [capacity][H]")
     if p.quant != QUANT_NONE:
@@ -342,41 +398,39 @@ def dispatch_fused(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.
         _need(recv.x.element_size() == 1, "FP8 codes are bytes")
     else:
         _need(recv.x.element_size() == 2, "bf16 rows")
-    cl, cr = layout.c(), recv.c()
-    _check(lib().ep_dispatch_fused(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl), _ptr(x),
-                                   ctypes.byref(cr), _ptr(ws), ws.numel(), _stream(stream)),
-           "ep_dispatch_fused")
+
+
+def _dispatch_fused_args(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
+                         recv: Recv, ws: torch.Tensor) -> _Args:
+    _check_fused(p, topk_idx, layout, x, recv)
+    _need(ws.numel() >= workspace_bytes(p), "workspace too small")
+    pc, cl, cr = p.c(), layout.c(), recv.c()
+    return _Args("ep_dispatch_fused", (ctypes.byref(pc), _ptr(topk_idx), ctypes.byref(cl), _ptr(x),
+                                       ctypes.byref(cr), _ptr(ws), ws.numel()), (pc, cl, cr))
 
 
 def dispatch_fused_noalloc(p: Problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
                            recv: Recv, stream=None) -> None:
     """dispatch_fused with the library's fixed scratch array instead of a
     workspace (ep_dispatch_fused_noalloc): nothing is allocated."""
-    R, T, H, E, K = p.R, p.T, p.H, p.E, p.K
-    _need(p.mode in (MODE_NORMAL, MODE_LOW_LATENCY), "normal or low-latency problem")
-    _need(topk_idx.dtype == torch.int32 and topk_idx.numel() == R * T * K, "topk_idx [R][T][K] int32")
-    _need(layout.num_tokens_per_expert.numel() == R * E and layout.is_token_in_rank.numel() == R * T * R,
-          "layout buffers do not match the problem")
-    _need(layout.send_pos is not None and layout.send_pos.numel() == R * T * K, "send_pos [R][T][K]")
-    _need(layout.send_head is None or layout.send_head.numel() == R * T * R, "send_head [R][T][R]")
-    _need(layout.recv_src_idx is None or layout.recv_src_idx.numel() >= layout.recv_capacity,
-          "recv_src_idx smaller than recv_capacity")
-    _need(x.dtype == torch.bfloat16 and x.numel() == R * T * H, "x [R][T][H] bf16")
-    _need(recv.x.shape[0] >= recv.capacity and recv.x.shape[1] == H, "recv x [capacity][H]")
-    if p.quant != QUANT_NONE:
-        n = p.G * (E * R * T if p.mode == MODE_LOW_LATENCY else recv.capacity)
-        _need(recv.scales is not None and recv.scales.numel() >= n, "recv scales")
-        _need(recv.x.element_size() == 1, "FP8 codes are bytes")
-    else:
-        _need(recv.x.element_size() == 2, "bf16 rows")
-    cl, cr = layout.c(), recv.c()
-    _check(lib().ep_dispatch_fused_noalloc(ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(cl),
-                                           _ptr(x), ctypes.byref(cr), _stream(stream)),
-           "ep_dispatch_fused_noalloc")
+    _invoke(_dispatch_fused_noalloc_args(p, topk_idx, layout, x, recv), stream)
+
+
+def _dispatch_fused_noalloc_args(p: Problem, topk_idx: torch.Tensor, layout: Layout,
+                                 x: torch.Tensor, recv: Recv) -> _Args:
+    _check_fused(p, topk_idx, layout, x, recv)
+    pc, cl, cr = p.c(), layout.c(), recv.c()
+    return _Args("ep_dispatch_fused_noalloc", (ctypes.byref(pc), _ptr(topk_idx), ctypes.byref(cl),
+                                               _ptr(x), ctypes.byref(cr)), (pc, cl, cr))
 
 
 def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,
             out: torch.Tensor, stream=None) -> None:
+    _invoke(_combine_args(p, layout, y, topk_weights, out), stream)
+
+
+def _combine_args(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,
+                  out: torch.Tensor) -> _Args:
     R, T, H, K = p.R, p.T, p.H, p.K
     _need(y.dtype == torch.bfloat16 and y.dim() == 2 and y.shape[1] == H, "y [rows][H] bf16")
     if p.mode != MODE_RANK_MAJOR or topk_weights is not None:
@@ -386,24 +440,32 @@ def combine(p: Problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Ten
     _need(layout.send_pos is not None and layout.send_pos.numel() == R * T * K, "send_pos")
     cl = layout.c()
     y_rows = y.shape[0]
-    _check(lib().ep_combine(ctypes.byref(p.c()), ctypes.byref(cl), _ptr(y), y_rows,
-                            _ptr(topk_weights), _ptr(out), _stream(stream)), "ep_combine")
+    pc = p.c()
+    return _Args("ep_combine", (ctypes.byref(pc), ctypes.byref(cl), _ptr(y), y_rows,
+                                _ptr(topk_weights), _ptr(out)), (pc, cl))
 
 
 def messages_execute(p: Problem, msgs: Messages, recv_arena: torch.Tensor, err: torch.Tensor,
-                     stream=None) -> None:
+                     stream=None, publish_batch: int = 0) -> None:
     """Loopback delivery of the descriptors of `msgs` into `recv_arena`
-    (uint8; msgs.arena_base[1][R] bytes suffice).  Error bits are OR-ed
-    into err[0]."""
+    (uint8; msgs.arena_base[1][R] bytes suffice), flags published every
+    `publish_batch` messages per workgroup (0: all after a second launch).
+    Error bits are OR-ed into err[0]."""
+    _invoke(_messages_execute_args(p, msgs, recv_arena, err, publish_batch), stream)
+
+
+def _messages_execute_args(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
+                           err: torch.Tensor, publish_batch: int = 0) -> _Args:
     _need(p.mode == MODE_MESSAGES, "message-mode problem")
     _need(recv_arena.dtype == torch.uint8, "recv_arena bytes")
     _need(err.dtype == torch.int32 and err.numel() >= 1, "err int32")
     _need(msgs.table.numel() == p.R * p.R * 8 and msgs.arena_base.numel() == 2 * (p.R + 1),
           "message table / arena bases")
-    cm = msgs.c()
-    _check(lib().ep_messages_execute(ctypes.byref(p.c()), ctypes.byref(cm), _ptr(recv_arena),
-                                     recv_arena.numel(), _ptr(err), _stream(stream)),
-           "ep_messages_execute")
+    _need(publish_batch >= 0, "publish_batch >= 0")
+    pc, cm = p.c(), msgs.c()
+    return _Args("ep_messages_execute", (ctypes.byref(pc), ctypes.byref(cm), _ptr(recv_arena),
+                                         recv_arena.numel(), int(publish_batch), _ptr(err)),
+                 (pc, cm))
 
 
 def unpack_buffers(p: Problem, device="cuda") -> tuple[Recv, torch.Tensor, torch.Tensor]:
@@ -418,10 +480,19 @@ def unpack_buffers(p: Problem, device="cuda") -> tuple[Recv, torch.Tensor, torch
 
 def messages_unpack(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
                     num_tokens_per_expert: torch.Tensor, out: Recv, recv_count: torch.Tensor,
-                    recv_src_idx: torch.Tensor, err: torch.Tensor, stream=None) -> None:
-    """Receiver: checks every delivered message and unpacks it into the
-    low-latency layout `out` (capacity >= E*R*T).  Error bits are OR-ed into
-    err[0]."""
+                    recv_src_idx: torch.Tensor, err: torch.Tensor, stream=None,
+                    spin_limit: int = 0) -> None:
+    """Receiver: checks every delivered message (polling its flag up to
+    `spin_limit` times first) and unpacks it into the low-latency layout
+    `out` (capacity >= E*R*T).  Error bits are OR-ed into err[0]."""
+    _invoke(_messages_unpack_args(p, msgs, recv_arena, num_tokens_per_expert, out, recv_count,
+                                  recv_src_idx, err, spin_limit), stream)
+
+
+def _messages_unpack_args(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
+                          num_tokens_per_expert: torch.Tensor, out: Recv, recv_count: torch.Tensor,
+                          recv_src_idx: torch.Tensor, err: torch.Tensor,
+                          spin_limit: int = 0) -> _Args:
     R, T, E = p.R, p.T, p.E
     rows = E * R * T
     _need(p.mode == MODE_MESSAGES, "message-mode problem")
@@ -437,11 +508,17 @@ def messages_unpack(p: Problem, msgs: Messages, recv_arena: torch.Tensor,
     _need(recv_src_idx.dtype == torch.int32 and recv_src_idx.numel() >= rows, "recv_src_idx")
     _need(err.dtype == torch.int32 and err.numel() >= 1, "err int32")
     _need(msgs.table.numel() == R * R * 8, "message table")
-    cm, cr = msgs.c(), out.c()
-    _check(lib().ep_messages_unpack(ctypes.byref(p.c()), ctypes.byref(cm), _ptr(recv_arena),
-                                    recv_arena.numel(), _ptr(num_tokens_per_expert),
-                                    ctypes.byref(cr), _ptr(recv_count), _ptr(recv_src_idx),
-                                    _ptr(err), _stream(stream)), "ep_messages_unpack")
+    pc, cm, cr = p.c(), msgs.c(), out.c()
+    return _Args("ep_messages_unpack", (ctypes.byref(pc), ctypes.byref(cm), _ptr(recv_arena),
+                                        recv_arena.numel(), _ptr(num_tokens_per_expert),
+                                        ctypes.byref(cr), _ptr(recv_count), _ptr(recv_src_idx),
+                                        int(spin_limit), _ptr(err)), (pc, cm, cr))
+
+
+_ARGS = {get_layout: _get_layout_args, dispatch: _dispatch_args,
+         dispatch_fused: _dispatch_fused_args, dispatch_fused_noalloc: _dispatch_fused_noalloc_args,
+         combine: _combine_args, messages_execute: _messages_execute_args,
+         messages_unpack: _messages_unpack_args}
 
 
 def messages_sizes(p: Problem, counts=None) -> tuple[int, int, int]:

@@ -285,15 +285,28 @@ int ep_combine(const ep_problem* p, const ep_layout* layout, const uint16_t* y,
  * (lkey >> 16)'s send arena to byte raddr of rank (rkey >> 16)'s receive
  * arena, the arena bases taken from m->arena_base (receive arena of rank d
  * = recv_arena[arena_base[1][d] ...]).  The last descriptor of every
- * message (m->table: first index + count - 1), its completion flag, is
- * copied in a second launch, after every payload and header.
+ * message (m->table: first index + count - 1) is its completion flag.
  * recv_arena: [recv_capacity] bytes, 16-byte aligned (arena_base[1][R]
  * bytes suffice).  Errors are OR-ed into *err (not reset):
  * EP_DEVERR_MESSAGE for a rank outside [0, R), EP_DEVERR_CAPACITY for a put
  * past either rank's arena or either buffer; such a put is skipped.
- * p->mode must be EP_MODE_MESSAGES. */
+ * p->mode must be EP_MODE_MESSAGES.
+ * publish_batch: when the flags go out (same page, Doorbell Batching and
+ * Sharing a QP; "ibgda_device.cuh" notes, sec. 4: a doorbell after every
+ * few requests).  0: every flag in a second launch, after every payload and
+ * header of the call.  B >= 1: one launch; each workgroup takes a run of
+ * messages in reservation order (the table's (source, destination) order)
+ * and, after every B of them and after its last, releases their payloads
+ * and headers with a device-scope fence and then writes their flags; a
+ * workgroup's batches are announced in order and no workgroup waits for
+ * another.  The delivered bytes are the same for every value; < 0 returns
+ * EP_ERR_SHAPE. */
 int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv_arena,
-                        int64_t recv_capacity, int32_t* err, void* stream);
+                        int64_t recv_capacity, int32_t publish_batch, int32_t* err,
+                        void* stream);
+
+/* Most polls ep_messages_unpack makes of one flag (spin_limit). */
+#define EP_MAX_SPIN (1 << 24)
 
 /* Receiver ("Eaas_server" notes; "DeepEP" sec. 1.2 and 2.1).  For every
  * (s, d) with a message (m->table[s][d]: token count n > 0), checks the
@@ -313,11 +326,19 @@ int ep_messages_execute(const ep_problem* p, const ep_messages* m, uint8_t* recv
  * num_tokens_per_expert: [R][E] (ep_get_layout's).  m->arena_base, when
  * not NULL, only chooses the block order from the receive loads (results
  * are the same either way).  p->mode must be EP_MODE_MESSAGES (p->quant,
- * p->epoch describe the messages). */
+ * p->epoch describe the messages).
+ * spin_limit in [0, EP_MAX_SPIN]: 0 checks each flag once (the delivery
+ * must have completed, e.g. ordered before on the same stream); n > 0
+ * first polls the flag with acquire loads ("GPU-Initiated Communication:
+ * Dissecting Down to the Bone", Ordering: the flag store is the last to
+ * become visible) up to n times, sleeping about 0.2 us between polls, and
+ * then checks; a flag still missing sets EP_DEVERR_MESSAGE.  The wait is
+ * bounded, so a delivery that never comes ends the call with the error
+ * rather than a hang. */
 int ep_messages_unpack(const ep_problem* p, const ep_messages* m, const uint8_t* recv_arena,
                        int64_t recv_capacity, const int32_t* num_tokens_per_expert,
                        const ep_recv* out, int32_t* recv_count, int32_t* recv_src_idx,
-                       int32_t* err, void* stream);
+                       int32_t spin_limit, int32_t* err, void* stream);
 
 /* Static text for a status code. */
 const char* ep_status_string(int status);

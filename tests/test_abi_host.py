@@ -109,19 +109,26 @@ def test_argument_errors_return_before_launch():
                            None, base16, ws_n, None) == -1
     # loopback execution and unpack: mode, NULL and capacity checks
     cm = ep.CMessages(base16, 64, base16, base16, base16, 1, base16)
-    assert lib.ep_messages_execute(ctypes.byref(p.c()), ctypes.byref(cm), base16, 64, base16,
+    assert lib.ep_messages_execute(ctypes.byref(p.c()), ctypes.byref(cm), base16, 64, 0, base16,
                                    None) == -4
-    assert lib.ep_messages_execute(ctypes.byref(pm.c()), ctypes.byref(cm), None, 64, base16,
+    assert lib.ep_messages_execute(ctypes.byref(pm.c()), ctypes.byref(cm), None, 64, 0, base16,
                                    None) == -1
-    assert lib.ep_messages_execute(ctypes.byref(pm.c()), ctypes.byref(cm), base16 + 8, 64, base16,
-                                   None) == -2
+    assert lib.ep_messages_execute(ctypes.byref(pm.c()), ctypes.byref(cm), base16 + 8, 64, 0,
+                                   base16, None) == -2
+    # a negative publication batch
+    assert lib.ep_messages_execute(ctypes.byref(pm.c()), ctypes.byref(cm), base16, 64, -1, base16,
+                                   None) == -3
     rows = 8 * 2 * 8
     ro = ep.CRecv(base16, base16, rows - 1)
     assert lib.ep_messages_unpack(ctypes.byref(pm.c()), ctypes.byref(cm), base16, 64, base16,
-                                  ctypes.byref(ro), base16, base16, base16, None) == -6
+                                  ctypes.byref(ro), base16, base16, 0, base16, None) == -6
     ro = ep.CRecv(base16, base16, rows)
     assert lib.ep_messages_unpack(ctypes.byref(pm.c()), ctypes.byref(cm), base16, 64, None,
-                                  ctypes.byref(ro), base16, base16, base16, None) == -1
+                                  ctypes.byref(ro), base16, base16, 0, base16, None) == -1
+    # a spin limit outside [0, 2^24]
+    for spin in (-1, (1 << 24) + 1):
+        assert lib.ep_messages_unpack(ctypes.byref(pm.c()), ctypes.byref(cm), base16, 64, base16,
+                                      ctypes.byref(ro), base16, base16, spin, base16, None) == -3
 
 
 def _oracle_sizes(R, T, H, E, K, quant, rb, topk):

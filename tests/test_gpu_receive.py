@@ -37,8 +37,10 @@ CASES = [
 FILL = 0x5C
 
 
-def run_gpu(w, p, topk, x, wt):
-    """Layout, pack, execute and unpack on the GPU; returns every buffer."""
+def run_gpu(w, p, topk, x, wt, publish_batch=0, spin_limit=0):
+    """Layout, pack, execute (flags published every `publish_batch`
+    messages, 0: after a second launch) and unpack (polling each flag up to
+    `spin_limit` times) on the GPU; returns every buffer."""
     gl, ws = gpu_layout(p, topk)
     send_cap, desc_cap = ep.messages_capacity(p, h(gl.num_tokens_per_rank))
     msgs = ep.Messages(p, send_cap, desc_cap)
@@ -50,12 +52,13 @@ def run_gpu(w, p, topk, x, wt):
     recv_cap = int(h(msgs.arena_base)[1, -1])
     arena = torch.full((recv_cap + 64,), 0xA5, dtype=torch.uint8, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ep.messages_execute(p, msgs, arena[:recv_cap], err)
+    ep.messages_execute(p, msgs, arena[:recv_cap], err, publish_batch=publish_batch)
     out, cnt, src = ep.unpack_buffers(p)
     out.x.view(torch.uint8).fill_(FILL)
     if out.scales is not None:
         out.scales.view(torch.uint8).fill_(FILL)
-    ep.messages_unpack(p, msgs, arena[:recv_cap], gl.num_tokens_per_expert, out, cnt, src, err)
+    ep.messages_unpack(p, msgs, arena[:recv_cap], gl.num_tokens_per_expert, out, cnt, src, err,
+                       spin_limit=spin_limit)
     torch.cuda.synchronize()
     return gl, ws, msgs, arena, recv_cap, out, cnt, src, err
 
@@ -85,9 +88,9 @@ def test_execute_and_unpack_match_oracle(case):
     check_case(case)
 
 
-def check_case(case, **kw):
+def check_case(case, publish_batch=0, spin_limit=0, **kw):
     name, R, T, H, E, K, quant, rb, mfrac, dfrac = case
-    say("receive", name)
+    say("receive", name, publish_batch, spin_limit)
     w = inputs.small(f"recv_{name}", R=R, T=T, H=H, E=E, K=K, mode=ep.MODE_MESSAGES, quant=quant,
                      seed=61, region_bytes=rb, epoch=5, **kw)
     topk = inputs.gen_topk(w)
@@ -95,7 +98,8 @@ def check_case(case, **kw):
         topk = inputs.masked_topk(w, topk, mfrac, dfrac, seed=3)
     x, wt = inputs.gen_x(w), inputs.gen_weights(w)
     p, po = problems(w)
-    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt)
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt, publish_batch,
+                                                                spin_limit)
     om, oarena, e1, u = oracle_side(w, po, topk, x, wt, msgs.send_capacity, msgs.desc_capacity,
                                     recv_cap, h(gl.num_tokens_per_expert))
     assert e1 == 0
@@ -115,6 +119,48 @@ def check_case(case, **kw):
     assert torch.equal(cnt, ll.recv_tokens_per_expert)
     assert int(h(ll.err)[0]) == int(h(err)[0])
     return h(msgs.arena_base)
+
+
+BATCH_CASES = [c for c in CASES if c[0] in ("r2_small_regions", "r4_ue8m0", "r8_wide", "r16_many_local",
+                                            "r4_bf16_dups", "r256")]
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 32])
+@pytest.mark.parametrize("case", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
+def test_batched_publication_delivers_the_same_bytes(case, batch):
+    """Flags published every 1, 2, 4 or 32 messages per workgroup, in one
+    launch: the receive arena and the unpacked layout equal the oracle's
+    (which delivers in no particular order) byte for byte, and the receiver
+    polls each flag (at most 1,000 times) before checking it."""
+    check_case(case, publish_batch=batch, spin_limit=1000)
+
+
+def test_polling_receiver_gives_up_on_a_missing_flag():
+    """A message whose flag never shows the epoch: the receiver polls it 16
+    times, gives up with the message bit and leaves that message's rows
+    untouched; every other message is unpacked as the oracle does."""
+    w = inputs.small("recv_spin", R=4, T=20, H=256, E=16, K=4, mode=ep.MODE_MESSAGES,
+                     quant=ep.QUANT_FP8_F32, seed=73, region_bytes=512, epoch=9)
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    gl, ws, msgs, arena, recv_cap, out, cnt, src, err = run_gpu(w, p, topk, x, wt, 4, 16)
+    assert int(h(err)[0]) == 0
+    table = h(msgs.table)
+    t21 = table[2, 1]
+    assert t21[3] > 0
+    bad = arena.clone()
+    bad[int(t21[1] + 16 + t21[4])] ^= 0x40  # the flag's epoch word never arrives
+    out2, cnt2, src2 = ep.unpack_buffers(p)
+    out2.x.fill_(FILL)
+    out2.scales.view(torch.uint8).fill_(FILL)
+    err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_unpack(p, msgs, bad[:recv_cap], gl.num_tokens_per_expert, out2, cnt2, src2, err2,
+                       spin_limit=16)
+    torch.cuda.synchronize()
+    u = orc.messages_unpack(po, h(bad)[:recv_cap], table, h(gl.num_tokens_per_expert),
+                            fill_codes=FILL)
+    assert u.err == orc.ERR_MESSAGE and int(h(err2)[0]) == ep.DEVERR_MESSAGE
+    compare_unpacked(w, out2, cnt2, src2, u)
 
 
 @pytest.mark.parametrize("alpha,skewed", [(None, False), (2.5, True)], ids=["uniform", "zipf"])
