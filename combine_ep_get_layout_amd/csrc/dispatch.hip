@@ -507,44 +507,6 @@ __global__ __launch_bounds__(256) void scales_from_tokens(const uint8_t* __restr
   }
 }
 
-// Low-latency FP8 scales from the per-token staging ("DeepEP" deep dive,
-// sec. 1.2: column-major scales per expert, [E][G][R*T]): block (e, tile)
-// takes the expert's slots [tile * kLLTile, ...) below its receive count,
-// reads each slot's token from recv_src_idx and writes the tile's part of
-// every column (e, g), consecutive threads on consecutive slots.  The ~32
-// slots an expert receives at the decode shape then fill their 128-byte
-// column line from one block, instead of 4 bytes at a time from 32 token
-// blocks on several dies.  Slots past the count are not written.
-constexpr int kLLTile = 256;
-
-template <int SB>
-__global__ __launch_bounds__(256) void scales_ll_from_tokens(const uint8_t* __restrict__ stage,
-                                                             uint8_t* __restrict__ scales, int G,
-                                                             int rt,
-                                                             const int32_t* __restrict__ count,
-                                                             const int32_t* __restrict__ row_token,
-                                                             int n_tok) {
-  __shared__ int tok[kLLTile];
-  const int e = blockIdx.x;
-  const int p0 = blockIdx.y * kLLTile;
-  const int n = min(count[e], rt);  // positions past R*T were refused by the layout
-  if (p0 >= n) return;
-  const int np = min(kLLTile, n - p0);
-  for (int q = threadIdx.x; q < np; q += blockDim.x) {
-    const int t = row_token[(int64_t)e * rt + p0 + q];
-    tok[q] = t >= 0 && t < n_tok ? t : -1;  // a token index out of range reads nothing
-  }
-  __syncthreads();
-  for (int it = threadIdx.x; it < G * np; it += blockDim.x) {
-    const int g = it / np, q = it - g * np;
-    const int t = tok[q];
-    if (t < 0) continue;
-    const int64_t di = ((int64_t)e * G + g) * rt + p0 + q;
-    if (SB == 4) ((uint32_t*)scales)[di] = ((const uint32_t*)stage)[(int64_t)t * G + g];
-    else scales[di] = stage[(int64_t)t * G + g];
-  }
-}
-
 inline RowMeta row_meta(const DispatchArgs& a) {
   RowMeta m;
   m.topk = a.topk;
@@ -603,8 +565,8 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
   // stay below both
   const int64_t cap = LL ? a.cap : (a.cap < a.stage_rows ? a.cap : a.stage_rows);
   const int blocks = LL ? xcd_blocks(N) : N;
-  const bool tok_stage = a.row_token != nullptr;
-  void* sc = LL && !tok_stage ? a.recv_scales : a.stage;
+  const bool tok_stage = !LL && a.row_token != nullptr;
+  void* sc = LL ? a.recv_scales : a.stage;  // low-latency scales go in place
   if (a.fused && !RM)
     hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, false, true>), dim3(fused_blocks(a, blocks)),
                        dim3(kWave * waves), 0, st, (const u32x4*)a.x, a.send_pos,
@@ -614,16 +576,6 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
     hipLaunchKernelGGL((dispatch_fp8<NP, Q, LL, RM, false>), dim3(blocks), dim3(kWave * waves),
                        0, st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, sc, P, a.g.K,
                        cap, a.g.G, a.g.R * a.g.T, N, a.err, row_meta(a), a.la, tok_stage);
-  if (LL && tok_stage) {
-    const int rt = a.g.R * a.g.T;
-    const dim3 grid((unsigned)a.g.E, (unsigned)((rt + kLLTile - 1) / kLLTile));
-    if (Q == EP_QUANT_FP8_F32)
-      hipLaunchKernelGGL(scales_ll_from_tokens<4>, grid, dim3(256), 0, st, (const uint8_t*)a.stage,
-                         (uint8_t*)a.recv_scales, a.g.G, rt, a.recv_per_expert, a.row_token, N);
-    else
-      hipLaunchKernelGGL(scales_ll_from_tokens<1>, grid, dim3(256), 0, st, (const uint8_t*)a.stage,
-                         (uint8_t*)a.recv_scales, a.g.G, rt, a.recv_per_expert, a.row_token, N);
-  }
   if (!LL) {
     // 256 rows per tile, fewer for wide rows (the tile lives in LDS), at
     // least 16 (16-byte aligned tiles)

@@ -110,10 +110,6 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
                              : entries + (int64_t)E * (p->expert_alignment - 1);
     off += up256((size_t)rows * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
   }
-#ifdef EP_LL_TOKEN_SCALES
-  if (p->mode == EP_MODE_LOW_LATENCY && p->quant != EP_QUANT_NONE)  // one row per token
-    off += up256((size_t)R * T * g->G * (p->quant == EP_QUANT_FP8_F32 ? 4 : 1));
-#endif
   g->ws_bytes = off < 256 ? 256 : off;
   return EP_OK;
 }
@@ -306,17 +302,8 @@ int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layou
   if (p->mode == EP_MODE_LOW_LATENCY && recv->capacity < (int64_t)g.E * g.R * g.T)
     return EP_ERR_CAPACITY;
   const bool rank_major = p->mode == EP_MODE_RANK_MAJOR;
-  const int64_t ll_rows = (int64_t)g.E * g.R * g.T;
-#ifdef EP_LL_TOKEN_SCALES
-  // low-latency FP8 with the layout's row -> token map: scales staged per
-  // token, then gathered into the column-major per-expert array
-  const bool ll_tok = p->mode == EP_MODE_LOW_LATENCY && p->quant != EP_QUANT_NONE &&
-                      layout->recv_src_idx && layout->recv_capacity >= ll_rows;
-#else
-  const bool ll_tok = false;
-#endif
   const bool staged =
-      ((p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE) || ll_tok;
+      (p->mode == EP_MODE_NORMAL || rank_major) && p->quant != EP_QUANT_NONE;
   if (rank_major && toks) {
     // per-row metadata needs the routing (ids) and, for weights, the weights
     if ((recv->topk_idx || recv->topk_weights) && !topk_idx) return EP_ERR_NULL;
@@ -341,8 +328,7 @@ int dispatch_args(const ep_problem* p, const Geometry& g, const ep_layout* layou
                             : (int64_t)g.R * g.T * g.K + (int64_t)g.E * (p->expert_alignment - 1);
   // scales staged once per token when the layout's row -> token map covers
   // every receive row (the staging holds stage_rows >= R*T rows either way)
-  const int64_t map_rows = p->mode == EP_MODE_LOW_LATENCY ? ll_rows : recv->capacity;
-  a->row_token = staged && layout->recv_src_idx && layout->recv_capacity >= map_rows
+  a->row_token = staged && layout->recv_src_idx && layout->recv_capacity >= recv->capacity
                      ? layout->recv_src_idx
                      : nullptr;
   a->align = p->mode == EP_MODE_NORMAL ? p->expert_alignment : 1;

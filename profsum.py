@@ -98,7 +98,7 @@ def main():
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     if args.json and traffic:
-        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
         from bench import kernel_hash
 
         d = {}
