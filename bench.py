@@ -370,7 +370,7 @@ class Runner:
         del scratch
         return t
 
-    def report(self, steps, warmup, extra=True, probes=None):
+    def report(self, steps, warmup, extra=True):
         w = self.w
         log(f"[bench] {w.name}: timing {steps} steps after {warmup} warm-up")
         ms, ph = self.run(steps, warmup)
@@ -410,20 +410,11 @@ class Runner:
         }
         if traffic is not None:  # counted HBM bytes over the same launch time
             res["roofline"]["traffic_GBps"] = round(traffic / (mean_ph[dom] * 1e-3) / 1e9, 1)
-        if probes is not None:
-            # the same reads and writes at the probes' read-only and
-            # write-only rates, taking turns: the measured roof for this mix
-            for k in phases:
-                phases[k]["frac_of_mix_ceiling"] = round(mix_ceiling(self.rw[k], probes)
-                                                         / mean_ph[k], 4)
-            rd = sum(r for r, _ in self.rw.values())
-            wr = sum(x for _, x in self.rw.values())
-            at = sum(mix_ceiling(v, probes) for v in self.rw.values())
-            res["mix_ceiling"] = {"read_bytes": rd, "written_bytes": wr,
-                                  "ms_at_probe_roofs": round(at, 4),
-                                  "GBps": round(total / (at * 1e-3) / 1e9, 1),
-                                  "frac": round(at / ms, 4)}
-            res["roofline"]["frac_of_mix_ceiling"] = phases[dom]["frac_of_mix_ceiling"]
+        # each phase's algorithmic bytes split into reads and writes (for
+        # the mix ceiling, added once the probes have run)
+        for k in phases:
+            phases[k]["read_bytes"], phases[k]["written_bytes"] = self.rw[k]
+        res["roofline"]["phase"] = dom
         # the calls after the layout alone (the bar's dispatch + combine)
         ms_nl = self.run_without_layout(steps) if extra else None
         if ms_nl is not None:
@@ -514,6 +505,25 @@ def mix_ceiling(rw, probes):
     reads and writes take turns: read / read rate + written / write rate."""
     r, wr = rw
     return (r / (probes["read_GBps"] * 1e9) + wr / (probes["write_GBps"] * 1e9)) * 1e3
+
+
+def add_mix_ceiling(res, probes):
+    """Adds to a workload's result the time its reads and writes take at the
+    probes' read-only and write-only rates, taking turns (the measured roof
+    for that mix of traffic), and the measured fraction of it: per phase,
+    for the roofline kernel's phase and for the whole step."""
+    phases = res["phases"]
+    at = 0.0
+    for v in phases.values():
+        c = mix_ceiling((v["read_bytes"], v["written_bytes"]), probes)
+        v["frac_of_mix_ceiling"] = round(c / v["ms_mean"], 4)
+        at += c
+    res["mix_ceiling"] = {"read_bytes": sum(v["read_bytes"] for v in phases.values()),
+                          "written_bytes": sum(v["written_bytes"] for v in phases.values()),
+                          "ms_at_probe_roofs": round(at, 4),
+                          "GBps": round(res["bytes_per_step"] / (at * 1e-3) / 1e9, 1),
+                          "frac": round(at / res["ms_per_step"], 4)}
+    res["roofline"]["frac_of_mix_ceiling"] = phases[res["roofline"]["phase"]]["frac_of_mix_ceiling"]
 
 
 def cpu_baseline(w, host, tokens_per_rank, min_seconds):
@@ -611,10 +621,6 @@ def main():
     from combine_ep_get_layout_amd import ep, inputs
 
     ep.lib()  # fail loudly if the HIP library is missing
-    probes = None
-    if not args.no_probes:
-        log("[bench] bandwidth probes")
-        probes = bandwidth_probes(torch)
     names = [n for n in args.workloads.split(",") if n]
     head = None
     others = {}
@@ -624,7 +630,7 @@ def main():
         fused = args.fused == "on" or (args.fused == "auto" and name in FUSED_WORKLOADS)
         r = Runner(w, torch, ep, inputs, keep_host=(i == 0 and not args.no_cpu), fused=fused)
         steps = args.steps if i == 0 else max(5, min(args.steps, 50))
-        ms, res = r.report(steps, args.warmup, extra=not args.no_extra, probes=probes)
+        ms, res = r.report(steps, args.warmup, extra=not args.no_extra)
         if i == 0:
             head = (w, ms, res)
             if not args.no_cpu:
@@ -640,6 +646,14 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
+    # the probes run after the workloads, so that their 4 GiB streams do not
+    # precede any timed step
+    probes = None
+    if not args.no_probes:
+        log("[bench] bandwidth probes")
+        probes = bandwidth_probes(torch)
+        for r_ in [head[2], *others.values()]:
+            add_mix_ceiling(r_, probes)
     w, ms, res = head
     if not args.no_cpu and w.mode != ep.MODE_MESSAGES:
         cpu = cpu_baseline(w, host, min(args.cpu_tokens or w.T, w.T), args.cpu_seconds)
