@@ -511,7 +511,9 @@ def add_mix_ceiling(res, probes):
     """Adds to a workload's result the time its reads and writes take at the
     probes' read-only and write-only rates, taking turns (the measured roof
     for that mix of traffic), and the measured fraction of it: per phase,
-    for the roofline kernel's phase and for the whole step."""
+    for the roofline kernel's phase and for the whole step; also the step's
+    rate as a fraction of the copy probe's (a stream that reads and writes
+    equal amounts at once)."""
     phases = res["phases"]
     at = 0.0
     for v in phases.values():
@@ -523,6 +525,8 @@ def add_mix_ceiling(res, probes):
                           "ms_at_probe_roofs": round(at, 4),
                           "GBps": round(res["bytes_per_step"] / (at * 1e-3) / 1e9, 1),
                           "frac": round(at / res["ms_per_step"], 4)}
+    if probes.get("copy_GBps"):
+        res["mix_ceiling"]["frac_of_copy_probe"] = round(res["GBps"] / probes["copy_GBps"], 4)
     res["roofline"]["frac_of_mix_ceiling"] = phases[res["roofline"]["phase"]]["frac_of_mix_ceiling"]
 
 

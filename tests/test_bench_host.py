@@ -93,14 +93,16 @@ def test_fp8_and_low_latency_bytes_match_the_closed_forms():
 def test_mix_ceiling_adds_read_and_write_times_at_the_probe_rates():
     # 7 GB read at 7 TB/s (1 ms) and 2 GB written at 4 TB/s (0.5 ms): a phase
     # measured at 2 ms runs at 0.75 of its mix ceiling
-    probes = {"read_GBps": 7000.0, "write_GBps": 4000.0}
+    probes = {"read_GBps": 7000.0, "write_GBps": 4000.0, "copy_GBps": 5000.0}
     assert abs(bench.mix_ceiling((7e9, 2e9), probes) - 1.5) < 1e-12
     res = {"phases": {"a": {"ms_mean": 2.0, "read_bytes": 7e9, "written_bytes": 2e9},
                       "b": {"ms_mean": 1.0, "read_bytes": 0, "written_bytes": 2e9}},
-           "bytes_per_step": 11e9, "ms_per_step": 4.0, "roofline": {"phase": "a"}}
+           "bytes_per_step": 11e9, "ms_per_step": 4.0, "GBps": 2750.0,
+           "roofline": {"phase": "a"}}
     bench.add_mix_ceiling(res, probes)
     assert res["phases"]["a"]["frac_of_mix_ceiling"] == 0.75
     assert res["phases"]["b"]["frac_of_mix_ceiling"] == 0.5
     assert res["mix_ceiling"]["ms_at_probe_roofs"] == 2.0
     assert res["mix_ceiling"]["frac"] == 0.5
     assert res["roofline"]["frac_of_mix_ceiling"] == 0.75
+    assert res["mix_ceiling"]["frac_of_copy_probe"] == 0.55
