@@ -36,7 +36,10 @@
  *    per token may be NULL when R*T == 0.  Struct arguments themselves are host memory,
  *    read during the call only.  The library allocates nothing, keeps no
  *    state between calls and is reentrant; calls that write the same
- *    buffers must not overlap.
+ *    buffers must not overlap.  (The one exception is
+ *    ep_dispatch_fused_noalloc, below: its scratch is a fixed array inside
+ *    the library, shared by every call on a GPU, whose device address is
+ *    looked up once per GPU and kept.)
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *    enqueued asynchronously on it; nothing is synchronised.
  *  - Return: EP_OK (0) or a negative EP_ERR_* code.  Argument errors are

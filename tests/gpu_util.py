@@ -2,6 +2,7 @@
 the CPU oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -11,6 +12,13 @@ from combine_ep_get_layout_amd import ep, inputs
 from oracle import oracle as orc
 
 DEV = "cuda"
+
+
+def sweep_cases(default: int) -> int:
+    """Random cases per drawer: `default`, or EP_SWEEP_CASES when set (a
+    wider sweep of the same drawers; the first `default` cases are the
+    suite's own)."""
+    return int(os.environ.get("EP_SWEEP_CASES", default))
 
 
 def say(*a):

@@ -8,7 +8,7 @@ import torch
 
 from combine_ep_get_layout_amd import ep, inputs
 from oracle import oracle as orc
-from gpu_util import DEV, LAYOUT_FIELDS, assert_layout_equal, h, say
+from gpu_util import DEV, LAYOUT_FIELDS, assert_layout_equal, h, say, sweep_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def draw(i):
             float(g.choice([0.0, 0.3])) if K > 1 else 0.0)
 
 
-FUZZ = [draw(i) for i in range(20)]
+FUZZ = [draw(i) for i in range(sweep_cases(20))]
 
 
 @pytest.mark.parametrize("c", CASES + FUZZ, ids=[c[0] for c in CASES + FUZZ])

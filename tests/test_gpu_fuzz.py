@@ -10,7 +10,7 @@ import torch
 from combine_ep_get_layout_amd import ep, inputs
 from oracle import oracle as orc
 from gpu_util import (DEV, abs_weighted_sum, assert_layout_equal, bf16_to_f32, combine_close,
-                      gpu_layout, h, problems, say)
+                      gpu_layout, h, problems, say, sweep_cases)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def draw(i):
                 dfrac=dfrac, rb=rb)
 
 
-CASES = [draw(i) for i in range(48)]
+CASES = [draw(i) for i in range(sweep_cases(48))]
 
 
 @pytest.mark.parametrize("i", range(len(CASES)))

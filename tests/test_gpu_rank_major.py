@@ -11,7 +11,7 @@ import torch
 
 from combine_ep_get_layout_amd import ep, inputs
 from oracle import oracle as orc
-from gpu_util import DEV, LAYOUT_FIELDS, bf16_to_f32, combine_close, h, say
+from gpu_util import DEV, LAYOUT_FIELDS, bf16_to_f32, combine_close, h, say, sweep_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ def draw(i):
             float(g.choice([0.0, 0.3])) if K > 1 else 0.0)
 
 
-CASES = FIXED + [draw(i) for i in range(16)]
+CASES = FIXED + [draw(i) for i in range(sweep_cases(16))]
 
 
 def run_case(c):

@@ -15,7 +15,7 @@ import torch
 
 from combine_ep_get_layout_amd import ep, inputs
 from oracle import oracle as orc
-from gpu_util import DEV, gpu_layout, h, problems, say
+from gpu_util import DEV, gpu_layout, h, problems, say, sweep_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -133,6 +133,32 @@ def test_batched_publication_delivers_the_same_bytes(case, batch):
     (which delivers in no particular order) byte for byte, and the receiver
     polls each flag (at most 1,000 times) before checking it."""
     check_case(case, publish_batch=batch, spin_limit=1000)
+
+
+def draw(i):
+    """A random message-mode case and publication batch (0: the two-launch
+    delivery): ranks, experts, top-k, tokens, payload format, hidden size,
+    region size (down to 64 bytes, so puts split), masked and duplicate ids."""
+    g = np.random.default_rng(9100 + i)
+    R = int(g.choice([1, 2, 3, 4, 5, 8, 16]))
+    E = R * int(g.integers(1, 9))
+    K = int(g.integers(1, min(E, 9) + 1))
+    T = int(g.choice([1, 7, 40, 100]))
+    quant = int(g.choice([ep.QUANT_NONE, ep.QUANT_FP8_F32, ep.QUANT_FP8_UE8M0]))
+    H = int(8 * g.integers(1, 100)) if quant == ep.QUANT_NONE else int(128 * g.integers(1, 9))
+    rb = int(g.choice([64, 256, 4096, 2 << 20]))
+    case = (f"fuzz{i}", R, T, H, E, K, quant, rb, float(g.choice([0.0, 0.2])),
+            float(g.choice([0.0, 0.3])) if K > 1 else 0.0)
+    return case, int(g.choice([0, 0, 1, 4, 32]))
+
+
+FUZZ = [draw(i) for i in range(sweep_cases(12))]
+
+
+@pytest.mark.parametrize("i", range(len(FUZZ)))
+def test_random_cases_match_oracle(i):
+    case, batch = FUZZ[i]
+    check_case(case, publish_batch=batch, spin_limit=1000 if batch else 0)
 
 
 def test_polling_receiver_gives_up_on_a_missing_flag():
