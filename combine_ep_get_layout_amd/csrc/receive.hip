@@ -96,7 +96,12 @@ __device__ inline void copy_range(const ExecArgs& a, const Put& p, int64_t lo, i
     const int64_t nv = (hi - lo) / 16;
     for (int64_t c0 = 0; c0 < nv; c0 += kCopyRound) {
       const int n = (int)min((int64_t)kCopyRound, nv - c0);
-      for (int j = threadIdx.x; j < n; j += blockDim.x) stage[j] = s4[c0 + j];
+      // non-temporal loads of the send arena (measured on MI355X at the
+      // 64-rank message workload: delivery 4% faster, the receiver after it
+      // 1% slower, the step 0.9% faster); plain stores (non-temporal ones
+      // made delivery 2% slower)
+      for (int j = threadIdx.x; j < n; j += blockDim.x)
+        stage[j] = __builtin_nontemporal_load(s4 + c0 + j);
       __syncthreads();
       for (int j = threadIdx.x; j < n; j += blockDim.x) d4[c0 + j] = stage[j];
       __syncthreads();
