@@ -331,6 +331,40 @@ class Runner:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
+    def run_separate_y(self, steps):
+        """The step with the combine reading a copy of the receive rows
+        made once (untimed) instead of the receive rows themselves: the
+        identity expert's output as a buffer of its own.  Returns the step
+        time (ms, as the headline) and the mean per-call event times; None
+        unless the expert output aliases the receive buffer (bf16 layouts)."""
+        torch = self.torch
+        if self.y is None or self.recv is None or self.y.data_ptr() != self.recv.x.data_ptr():
+            return None
+        self.y = self.recv.x.clone()
+        self._phases = None
+        try:
+            for _ in range(3):
+                self.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                self.step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            names = [n for n, _ in self.phases()]
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                   for _ in range(steps)]
+            for i in range(steps):
+                self.step(evs[i])
+            torch.cuda.synchronize()
+            ph = {k: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])), 4)
+                  for i, k in enumerate(names)}
+        finally:
+            self.y = self.recv.x
+            self._phases = None
+            torch.cuda.empty_cache()
+        return ms, ph
+
     def publish_curve(self, reps=20, batches=(0, 1, 4, 32)):
         """Delivery time (ms, mean of `reps` back-to-back calls, events
         around them) for each publication batch: 0 = every flag after a
@@ -424,6 +458,15 @@ class Runner:
                                      "GBps": round(b / (ms_nl * 1e-3) / 1e9, 1),
                                      "frac_of_peak": round(b / (ms_nl * 1e-3) / 1e9
                                                            / PEAK_HBM_GBPS, 4)}
+        # the same step with the expert output in a buffer of its own: the
+        # next dispatch then follows a combine that read other memory
+        sep = self.run_separate_y(steps) if extra else None
+        if sep is not None:
+            res["separate_expert_output"] = {
+                "note": "combine reads a copy of the receive rows made once, untimed",
+                "ms_per_step": round(sep[0], 4),
+                "GBps": round(total / (sep[0] * 1e-3) / 1e9, 1),
+                "phase_ms": sep[1]}
         res.update(self.extra)
         if self.msgs is not None and extra:
             res["execute_ms_by_publish_batch"] = self.publish_curve()
@@ -683,6 +726,7 @@ def main():
         "phases": res["phases"],
         "roofline": res["roofline"],
         "without_layout": res.get("without_layout"),
+        "separate_expert_output": res.get("separate_expert_output"),
         "mix_ceiling": res.get("mix_ceiling"),
         "bandwidth_probes": probes,
         "workloads": others,
