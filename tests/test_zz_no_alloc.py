@@ -3,8 +3,9 @@ the caller's workspace) against ep_dispatch_fused through the C ABI, bit for
 bit: two calls in a row on one stream, the second with a smaller problem
 (the array keeps the first call's contents), every layout output, receive
 row and scale compared; then the same pair again in the other order on a
-second stream; a problem needing more scratch than the array is refused
-before anything is enqueued."""
+second stream; the call captured into a HIP graph and replayed with fresh
+inputs; a problem needing more scratch than the array is refused before
+anything is enqueued."""
 import ctypes
 
 import numpy as np
@@ -77,6 +78,53 @@ def test_noalloc_on_a_second_stream():
     s = torch.cuda.Stream()
     check(SMALL, s)
     check(BIG, s)
+
+
+def test_noalloc_replays_in_a_graph():
+    """The entry point captured once into a HIP graph (the callers it is
+    for) and replayed with fresh routing and tokens copied into its inputs,
+    every output poisoned first: each replay equals an eager
+    ep_dispatch_fused of the same inputs, bit for bit."""
+    name, R, T, H, E, K, mode, quant, align, _, _ = BIG
+    p, po, topk, x = make(BIG)
+    tk = torch.from_numpy(topk).to(DEV)
+    xg = torch.from_numpy(x).view(torch.bfloat16).to(DEV)
+    lg, rg = outputs(p)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call = ep.prepare(ep.dispatch_fused_noalloc, p, tk, lg, xg, rg)
+        call()  # first call on the device (the array's address is looked up) outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        w = inputs.small(f"noalloc_graph_{rep}", R=R, T=T, H=H, E=E, K=K, mode=mode, quant=quant,
+                         seed=300 + rep)
+        topk_r = inputs.gen_topk(w)
+        if rep % 2 == 1:
+            topk_r = inputs.masked_topk(w, topk_r, 0.2, 0.0, seed=rep)
+        tk.copy_(torch.from_numpy(topk_r))
+        xg.copy_(torch.from_numpy(inputs.gen_x(w)).view(torch.bfloat16))
+        rg.x.view(torch.uint8).fill_(0x33)
+        rg.scales.view(torch.uint8).fill_(0x33)
+        lg.recv_src_idx.fill_(-7)
+        lg.send_pos.fill_(-7)
+        torch.cuda.synchronize()
+        say("noalloc graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        lf, rf = outputs(p)
+        ep.dispatch_fused(p, tk, lf, xg, rf, ep.workspace(p))
+        torch.cuda.synchronize()
+        for f in LAYOUT_FIELDS + ["err", "recv_src_idx"]:
+            assert torch.equal(getattr(lg, f), getattr(lf, f)), (rep, f)
+        assert torch.equal(rg.x, rf.x)
+        assert torch.equal(rg.scales, rf.scales)
+        assert_layout_equal(lg, orc.layout(po, topk_r), p.mode)
 
 
 def test_noalloc_refuses_problems_past_the_array():
