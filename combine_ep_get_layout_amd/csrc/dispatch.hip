@@ -14,8 +14,9 @@
 //  - wider bf16 rows, and FP8: one wavefront per piece of the row, held in
 //    registers (quantised once if asked), the whole row in flight at once.
 // (Measured on MI355X at hidden 7168: plain stores beat non-temporal ones
-// for this scatter; the kernel sits at the chip's write-dominated
-// bandwidth.)
+// for the bf16 scatter, and so they do for normal-mode FP8 codes; the
+// low-latency FP8 codes go out non-temporal, see dispatch_fp8.  The kernels
+// sit at the chip's write-dominated bandwidth.)
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 #include "layout_rows.hpp"
