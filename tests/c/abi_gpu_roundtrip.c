@@ -1,8 +1,9 @@
 /* A plain C caller of libep on the GPU, with device memory from the HIP
  * runtime and no Python: the layout, dispatch and combine of a small
  * normal-mode bf16 problem through ep_get_layout / ep_dispatch / ep_combine,
- * then the fused low-latency FP8 call (ep_dispatch_fused), each result
- * compared with the oracle's C functions (oracle/ep_oracle.h).  Built and
+ * then the fused low-latency FP8 call (ep_dispatch_fused), then message
+ * mode end to end (sizing, packer and descriptors, delivery, receiver),
+ * each result compared with the oracle's C functions (oracle/ep_oracle.h).  Built and
  * run by tests/test_gpu_c_roundtrip.py. */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -153,8 +154,10 @@ static void check_layout(const dev_layout* d, const orc_problem* op, const int32
   expect(same_i32(d->l.rows_per_rank, rows, R), what);
   snprintf(what, sizeof what, "%s: row_base", name);
   expect(same_i32(d->l.row_base, base, R + 1), what);
-  snprintf(what, sizeof what, "%s: send_pos", name);
-  expect(same_i32(d->l.send_pos, send_pos, R * T * K), what);
+  if (d->l.send_pos) { /* message mode's layout has no receive rows */
+    snprintf(what, sizeof what, "%s: send_pos", name);
+    expect(same_i32(d->l.send_pos, send_pos, R * T * K), what);
+  }
   snprintf(what, sizeof what, "%s: send_head", name);
   expect(same_i32(d->l.send_head, send_head, R * T * R), what);
   uint8_t* g_in = host_of(d->l.is_token_in_rank, (size_t)R * T * R);
@@ -162,13 +165,15 @@ static void check_layout(const dev_layout* d, const orc_problem* op, const int32
   expect(memcmp(g_in, in_rank, (size_t)R * T * R) == 0, what);
   free(g_in);
   /* filled rows: every row a routed entry names */
-  int32_t* g_src = host_of(d->l.recv_src_idx, sizeof(int32_t) * (size_t)cap);
-  int ok = 1;
-  for (int64_t i = 0; i < (int64_t)R * T * K; ++i)
-    if (send_pos[i] >= 0) ok &= g_src[send_pos[i]] == src_idx[send_pos[i]];
-  snprintf(what, sizeof what, "%s: recv_src_idx", name);
-  expect(ok, what);
-  free(g_src);
+  if (d->l.recv_src_idx) {
+    int32_t* g_src = host_of(d->l.recv_src_idx, sizeof(int32_t) * (size_t)cap);
+    int ok = 1;
+    for (int64_t i = 0; i < (int64_t)R * T * K; ++i)
+      if (send_pos[i] >= 0) ok &= g_src[send_pos[i]] == src_idx[send_pos[i]];
+    snprintf(what, sizeof what, "%s: recv_src_idx", name);
+    expect(ok, what);
+    free(g_src);
+  }
   *send_pos_out = send_pos;
   free(cnt_rank);
   free(cnt_expert);
@@ -348,6 +353,140 @@ static void ll_fp8_fused(void) {
   free(x);
 }
 
+/* message mode, FP8 with fp32 scales: packer and descriptors, loopback
+ * delivery, receiver; sizes from ep_messages_capacity on read-back counts */
+static void messages_path(void) {
+  const int R = 4, T = 40, H = 256, E = 16, K = 4, N = R * T, G = H / 128, RT = R * T;
+  ep_problem p = problem(R, T, H, E, K, EP_MODE_MESSAGES, EP_QUANT_FP8_F32);
+  p.region_bytes = 512; /* puts are cut at every 512-byte boundary */
+  p.epoch = 7;
+  orc_problem op = oproblem(&p);
+  int32_t* topk = malloc(sizeof(int32_t) * N * K);
+  uint16_t* x = malloc(sizeof(uint16_t) * (size_t)N * H);
+  float* w = malloc(sizeof(float) * N * K);
+  gen_routing(R, T, E, K, topk);
+  for (int64_t i = 0; i < (int64_t)N * H; ++i)
+    x[i] = to_bf16(((float)(next_u32() % 40001u) - 20000.0f) / 1000.0f);
+  for (int i = 0; i < N * K; ++i) w[i] = (float)(next_u32() % 1000u + 1u) / 1000.0f;
+  const size_t ws_bytes = ep_workspace_bytes(&p);
+  void* ws = dev(ws_bytes);
+  void* d_topk = dev(sizeof(int32_t) * N * K);
+  void* d_x = dev(sizeof(uint16_t) * (size_t)N * H);
+  void* d_w = dev(sizeof(float) * N * K);
+  HIP_OK(hipMemcpy(d_topk, topk, sizeof(int32_t) * N * K, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_x, x, sizeof(uint16_t) * (size_t)N * H, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_w, w, sizeof(float) * N * K, hipMemcpyHostToDevice));
+  dev_layout d;
+  layout_alloc(&d, R, T, E, K, 16);
+  HIP_OK(hipFree(d.l.send_pos));
+  HIP_OK(hipFree(d.l.recv_src_idx));
+  d.l.send_pos = NULL; /* message mode: no receive rows, only send_head */
+  d.l.recv_src_idx = NULL;
+  d.l.recv_capacity = 0;
+  expect(ep_get_layout(&p, d_topk, &d.l, ws, ws_bytes, NULL) == EP_OK, "messages: ep_get_layout");
+  HIP_OK(hipDeviceSynchronize());
+  int32_t* counts = host_of(d.l.num_tokens_per_rank, sizeof(int32_t) * R * R);
+  int64_t send_bytes = 0, recv_bytes = 0, ndesc = 0;
+  expect(ep_messages_capacity(&p, counts, &send_bytes, &recv_bytes, &ndesc) == EP_OK,
+         "messages: ep_messages_capacity");
+  ep_messages m;
+  memset(&m, 0, sizeof m);
+  m.send_arena = dev((size_t)send_bytes);
+  m.send_capacity = send_bytes;
+  m.table = dev(sizeof(int64_t) * R * R * 8);
+  m.arena_base = dev(sizeof(int64_t) * 2 * (R + 1));
+  m.descriptors = dev((size_t)ndesc * 64);
+  m.desc_capacity = ndesc;
+  m.num_descriptors = dev(sizeof(int64_t));
+  expect(ep_dispatch(&p, &d.l, d_x, d_topk, d_w, NULL, &m, ws, ws_bytes, NULL) == EP_OK,
+         "messages: ep_dispatch");
+  uint8_t* recv_arena = dev((size_t)recv_bytes);
+  int32_t* err = dev(sizeof(int32_t));
+  HIP_OK(hipMemset(err, 0, sizeof(int32_t)));
+  expect(ep_messages_execute(&p, &m, recv_arena, recv_bytes, 0, err, NULL) == EP_OK,
+         "messages: ep_messages_execute");
+  ep_recv out;
+  memset(&out, 0, sizeof out);
+  out.x = dev((size_t)E * RT * H);
+  out.scales = dev(sizeof(float) * (size_t)E * G * RT);
+  out.capacity = (int64_t)E * RT;
+  int32_t* d_count = dev(sizeof(int32_t) * E);
+  int32_t* d_src = dev(sizeof(int32_t) * E * RT);
+  expect(ep_messages_unpack(&p, &m, recv_arena, recv_bytes, d.l.num_tokens_per_expert, &out,
+                            d_count, d_src, 0, err, NULL) == EP_OK,
+         "messages: ep_messages_unpack");
+  HIP_OK(hipDeviceSynchronize());
+
+  int32_t* send_pos;
+  check_layout(&d, &op, topk, 0, &send_pos, "messages");
+  /* the oracle's packer, delivery and receiver */
+  uint8_t* o_send = calloc((size_t)send_bytes, 1);
+  int64_t* o_table = malloc(sizeof(int64_t) * R * R * 8);
+  int64_t* o_base = malloc(sizeof(int64_t) * 2 * (R + 1));
+  uint8_t* o_desc = calloc((size_t)ndesc, 64);
+  int64_t o_nd = 0;
+  expect(orc_messages(&op, x, topk, w, o_send, send_bytes, o_table, o_base, o_desc, ndesc,
+                      &o_nd) == 0, "messages: oracle packer");
+  int64_t* g_table = host_of(m.table, sizeof(int64_t) * R * R * 8);
+  int64_t* g_base = host_of(m.arena_base, sizeof(int64_t) * 2 * (R + 1));
+  int64_t* g_nd = host_of(m.num_descriptors, sizeof(int64_t));
+  uint8_t* g_desc = host_of(m.descriptors, (size_t)ndesc * 64);
+  uint8_t* g_send = host_of(m.send_arena, (size_t)send_bytes);
+  expect(memcmp(g_table, o_table, sizeof(int64_t) * R * R * 8) == 0, "messages: table");
+  expect(memcmp(g_base, o_base, sizeof(int64_t) * 2 * (R + 1)) == 0, "messages: arena bases");
+  expect(*g_nd == o_nd && o_nd == ndesc, "messages: descriptor count");
+  expect(memcmp(g_desc, o_desc, (size_t)o_nd * 64) == 0, "messages: descriptors");
+  int ok = 1;
+  for (int i = 0; i < R * R; ++i)
+    if (o_table[i * 8 + 2] > 0)
+      ok &= memcmp(g_send + o_table[i * 8], o_send + o_table[i * 8], (size_t)o_table[i * 8 + 2]) == 0;
+  expect(ok, "messages: message regions");
+  uint8_t* o_recv = calloc((size_t)recv_bytes, 1);
+  expect(orc_messages_execute(&op, o_send, send_bytes, o_base, o_desc, o_nd, o_recv, recv_bytes)
+             == 0, "messages: oracle delivery");
+  uint8_t* g_recv = host_of(recv_arena, (size_t)recv_bytes);
+  ok = 1;
+  for (int i = 0; i < R * R; ++i)
+    if (o_table[i * 8 + 2] > 0)
+      ok &= memcmp(g_recv + o_table[i * 8 + 1], o_recv + o_table[i * 8 + 1],
+                   (size_t)o_table[i * 8 + 2]) == 0;
+  expect(ok, "messages: delivered regions");
+  int32_t* cnt_expert = host_of(d.l.num_tokens_per_expert, sizeof(int32_t) * R * E);
+  uint8_t* o_codes = calloc((size_t)E * RT * H, 1);
+  float* o_scales = calloc((size_t)E * G * RT, sizeof(float));
+  int32_t* o_count = malloc(sizeof(int32_t) * E);
+  int32_t* o_src = malloc(sizeof(int32_t) * E * RT);
+  for (int i = 0; i < E * RT; ++i) o_src[i] = -1;
+  expect(orc_messages_unpack(&op, o_recv, recv_bytes, o_table, cnt_expert, o_codes, o_scales,
+                             o_count, o_src) == 0, "messages: oracle receiver");
+  int32_t* g_err = host_of(err, sizeof(int32_t));
+  expect(*g_err == 0, "messages: delivery and receiver error word");
+  expect(same_i32(d_count, o_count, E), "messages: receive counts");
+  uint8_t* g_codes = host_of(out.x, (size_t)E * RT * H);
+  float* g_scales = host_of(out.scales, sizeof(float) * (size_t)E * G * RT);
+  int32_t* g_src = host_of(d_src, sizeof(int32_t) * E * RT);
+  int ok_rows = 1, ok_sc = 1, ok_src = 1, filled = 0;
+  for (int r = 0; r < E * RT; ++r) {
+    if (o_src[r] < 0) continue;
+    ++filled;
+    ok_src &= g_src[r] == o_src[r];
+    ok_rows &= memcmp(g_codes + (int64_t)r * H, o_codes + (int64_t)r * H, H) == 0;
+    const int e = r / RT, pos = r % RT;
+    for (int g = 0; g < G; ++g) {
+      const int64_t si = ((int64_t)e * G + g) * RT + pos;
+      ok_sc &= memcmp(&g_scales[si], &o_scales[si], sizeof(float)) == 0;
+    }
+  }
+  expect(filled > 0, "messages: rows were unpacked");
+  expect(ok_src, "messages: unpacked source indices");
+  expect(ok_rows, "messages: unpacked codes");
+  expect(ok_sc, "messages: unpacked scales");
+  free(g_codes); free(g_scales); free(g_src); free(g_err); free(o_codes); free(o_scales);
+  free(o_count); free(o_src); free(cnt_expert); free(g_recv); free(o_recv); free(g_send);
+  free(g_desc); free(g_nd); free(g_base); free(g_table); free(o_desc); free(o_base);
+  free(o_table); free(o_send); free(counts); free(send_pos); free(topk); free(x); free(w);
+}
+
 int main(void) {
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
@@ -356,6 +495,7 @@ int main(void) {
   }
   normal_bf16();
   ll_fp8_fused();
+  messages_path();
   if (failures) {
     printf("%d checks failed\n", failures);
     return 1;

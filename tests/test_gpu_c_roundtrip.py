@@ -1,7 +1,8 @@
 """The C ABI driven end to end from plain C on the GPU: tests/c/abi_gpu_roundtrip.c
 allocates device memory with the HIP runtime, runs layout, dispatch and
-combine (normal mode, bf16) and the fused low-latency FP8 call through
-include/ep.h, and compares every output with the oracle's C functions.
+combine (normal mode, bf16), the fused low-latency FP8 call and message
+mode (sizing, packer, delivery, receiver) through include/ep.h, and compares
+every output with the oracle's C functions.
 Compiling it needs only the headers, so that part runs on the CPU too."""
 import os
 import shutil
