@@ -1,14 +1,17 @@
-"""Receive buffers past 2^31 sixteen-byte vectors (over 32 GiB), through the
-C ABI against the oracle: row addressing in the dispatch and combine
-kernels must be 64-bit, since a row index (int32) times the row's vectors
-overflows 32 bits there.
+"""Buffers past 32-bit offsets, through the C ABI against the oracle: receive
+buffers past 2^31 sixteen-byte vectors (over 32 GiB), where a row index
+(int32) times the row's vectors overflows 32 bits, and message arenas past
+4 GiB.
 
 - normal mode, bf16, hidden 7168, top-32 of 256 experts, 8 ranks x 9400
   tokens: 2,406,400 receive rows, 34.5 GB; the separate layout, dispatch
   and combine calls, the combine's kernel the prefill shape uses;
 - low-latency FP8 (fp32 scales) through the fused call, 8 ranks x 2400
   tokens, 256 experts: 4,915,200 slots, 35.2 GB of codes; the combine then
-  reads a 70.5 GB bf16 expert output in the same layout.
+  reads a 70.5 GB bf16 expert output in the same layout;
+- message mode with bf16 payloads, 8 ranks x 8192 tokens: send and receive
+  arenas of 5.1 GB (byte offsets past 32 bits) through packer, delivery
+  and receiver.
 
 Every layout output is compared whole; receive rows, codes and scales and
 the combined outputs on sampled tokens, among them the tokens whose rows
@@ -152,4 +155,72 @@ def test_low_latency_fp8_fused_slots_past_2_31_vectors():
     y[torch.from_numpy(rows.astype(np.int64)).to(DEV)] = torch.from_numpy(yc).view(torch.bfloat16).to(DEV)
     check_combine(w, p, po, lay, ol.send_pos, y, yc, rows, wt, toks)
     del y, lay
+    torch.cuda.empty_cache()
+
+
+def test_message_arenas_past_4_gib():
+    """Message mode, bf16 payloads, 8 ranks x 8192 tokens, 64 experts: send
+    and receive arenas over 4 GiB (byte offsets past 32 bits) in 2 MiB
+    regions.  The table, arena bases and every descriptor against the
+    oracle; every message region of the send arena and, after the loopback
+    delivery, of the receive arena; the receiver's counts, and its rows and
+    source indices on sampled tokens (an unpacked entry sits where
+    low-latency dispatch of the same routing puts it, and is its token's
+    row)."""
+    w = inputs.small("large_msg", R=8, T=8192, H=7168, E=64, K=8, mode=ep.MODE_MESSAGES,
+                     quant=ep.QUANT_NONE, seed=31)
+    need_memory(80 << 30)
+    say("large messages: inputs")
+    topk, x, wt = inputs.gen_topk(w), inputs.gen_x(w), inputs.gen_weights(w)
+    p, po = problems(w)
+    ol = orc.layout(po, topk)
+    gl, ws = gpu_layout(p, topk)
+    assert_layout_equal(gl, ol, w.mode)
+    send_cap, desc_cap = ep.messages_capacity(p, ol.num_tokens_per_rank)
+    assert send_cap > 1 << 32
+    msgs = ep.Messages(p, send_cap, desc_cap)
+    say("large messages: pack", send_cap, "bytes")
+    ep.dispatch(p, gl, torch.from_numpy(x).view(torch.bfloat16).to(DEV), msgs=msgs,
+                topk_idx=torch.from_numpy(topk).to(DEV), topk_weights=torch.from_numpy(wt).to(DEV),
+                ws=ws)
+    torch.cuda.synchronize()
+    assert int(h(gl.err)[0]) == 0
+    om = orc.messages(po, x, topk, wt, send_cap, desc_cap)
+    assert om.err == 0
+    assert np.array_equal(h(msgs.table), om.table)
+    assert np.array_equal(h(msgs.arena_base), om.arena_base)
+    assert int(h(msgs.num_descriptors)[0]) == om.num_desc
+    assert np.array_equal(h(msgs.descriptors)[:om.num_desc], om.desc)
+    sd = om.table.reshape(-1, 8)
+    for off, reg in sd[:, [0, 2]]:
+        if reg > 0:
+            assert np.array_equal(h(msgs.send_arena[off:off + reg]), om.send_arena[off:off + reg]), off
+    recv_cap = int(om.arena_base[1, -1])
+    assert recv_cap > 1 << 32
+    say("large messages: delivery", recv_cap, "bytes")
+    arena = torch.full((recv_cap,), 0xA5, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ep.messages_execute(p, msgs, arena, err)
+    torch.cuda.synchronize()
+    assert int(h(err)[0]) == 0
+    e1, oarena = orc.messages_execute(po, om, recv_cap)
+    assert e1 == 0
+    for off, reg in sd[:, [1, 2]]:
+        if reg > 0:
+            assert np.array_equal(h(arena[off:off + reg]), oarena[off:off + reg]), off
+    del oarena, om
+    say("large messages: receiver")
+    out, cnt, src = ep.unpack_buffers(p)
+    ep.messages_unpack(p, msgs, arena, gl.num_tokens_per_expert, out, cnt, src, err)
+    torch.cuda.synchronize()
+    assert int(h(err)[0]) == 0
+    oll = orc.layout(orc.Problem(w.R, w.T, w.H, w.E, w.K, mode=orc.MODE_LL), topk)
+    assert np.array_equal(h(cnt), oll.recv_tokens_per_expert)
+    toks = sample_tokens(oll.send_pos, w.K)
+    sp = oll.send_pos.reshape(-1, w.K)[toks]
+    xs = x.reshape(-1, w.H)[toks]
+    for k in range(w.K):
+        assert np.array_equal(rows_of(out.x, sp[:, k]), xs), k
+        assert np.array_equal(rows_of(src, sp[:, k]), toks.astype(np.int32)), k
+    del out, cnt, src, arena, msgs, gl, ws
     torch.cuda.empty_cache()
