@@ -21,11 +21,6 @@ namespace {
 #ifndef EP_LAYOUT_TARGET_CHUNKS
 #define EP_LAYOUT_TARGET_CHUNKS 1024
 #endif
-// most batches of entries per layout chunk: a count wavefront walks its
-// chunk's batches one after another (measured on MI355X at the FP8 training
-// shape, 16 batches per chunk: count 22.3 us + scan 4.9 us; 8 batches, twice
-// the chunks: 15.5 + 6.0 us; 4 batches: 13.7 + 11.5 us)
-constexpr int kMaxBatches = 8;
 #ifndef EP_DIRECT_MAX_ENTRIES
 #define EP_DIRECT_MAX_ENTRIES 6144
 #endif
@@ -88,7 +83,7 @@ int ep::make_geometry(const ep_problem* p, Geometry* g) {
   const int64_t batches = (int64_t)R * ((T + tb - 1) / tb);
   int64_t per = (batches + kTargetChunks - 1) / kTargetChunks;
   if (per < 1) per = 1;
-  if (per > kMaxBatches) per = kMaxBatches;
+  if (per > kMaxChunkBatches) per = kMaxChunkBatches;
   g->ct = tb * (int)per;
   g->C = (T + g->ct - 1) / g->ct;
   g->NC = R * g->C;
