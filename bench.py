@@ -493,8 +493,8 @@ def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
     thread (1, 2, 4, 8), plain or non-temporal accesses and three grid
     sizes; bytes moved / mean event time of `reps` launches on 4 GiB
     buffers.  These are the device's measured roofs for streams that only
-    read or only write, next to which the method's mix of reads and writes
-    is judged."""
+    read or only write, against which the method's mix of reads and
+    writes is measured."""
     import ctypes
 
     if not os.path.exists(PROBE_LIB):
