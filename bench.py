@@ -485,6 +485,8 @@ class Runner:
 
 PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
 PROBE_KINDS = {"read": 0, "write": 1, "copy": 2}
+# fan-out probe shape: row vectors (16 bytes each), rows, copies per row
+FANOUT_SHAPE = (896, 32768, 8)
 
 
 def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
@@ -537,9 +539,36 @@ def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
                         best = (rate, {"unroll": unroll, "nt": nt, "blocks": blocks})
         out[name + "_GBps"] = round(best[0], 1)
         out[name + "_config"] = best[1]
+    # the bf16 dispatch's mix at the prefill shape: 32,768 rows of 14,336
+    # bytes, each read once and written to 8 rows
+    lib.bench_fanout_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.bench_fanout_launch.restype = ctypes.c_int
+    fv, fr, fk = FANOUT_SHAPE
+    assert fr * fv * 16 <= nbytes and fk * fr * fv * 16 <= nbytes
+    best = (0.0, None)
+    for form in (0, 1):
+        def launch():
+            if lib.bench_fanout_launch(a.data_ptr(), b.data_ptr(), fv, fr, fk, form, stream) != 0:
+                raise RuntimeError("fan-out probe launch failed")
+
+        launch()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            launch()
+        e.record()
+        torch.cuda.synchronize()
+        rate = fr * fv * 16 * (1 + fk) / (s.elapsed_time(e) / reps * 1e-3) / 1e9
+        if rate > best[0]:
+            best = (rate, {"row_bytes": fv * 16, "rows": fr, "copies": fk, "form": form})
+    out["fanout_GBps"] = round(best[0], 1)
+    out["fanout_config"] = best[1]
     del a, b, sink
     torch.cuda.empty_cache()
-    out["source"] = "bench_probe.hip (16-byte vector streams, 4 GiB buffers)"
+    out["source"] = ("bench_probe.hip (16-byte vector streams, 4 GiB buffers; fan-out: each row "
+                     "read once and written to `copies` contiguous segments)")
     return out
 
 
@@ -550,7 +579,7 @@ def mix_ceiling(rw, probes):
     return (r / (probes["read_GBps"] * 1e9) + wr / (probes["write_GBps"] * 1e9)) * 1e3
 
 
-def add_mix_ceiling(res, probes):
+def add_mix_ceiling(res, probes, w=None):
     """Adds to a workload's result the time its reads and writes take at the
     probes' read-only and write-only rates, taking turns (the measured roof
     for that mix of traffic), and the measured fraction of it: per phase,
@@ -571,6 +600,13 @@ def add_mix_ceiling(res, probes):
     if probes.get("copy_GBps"):
         res["mix_ceiling"]["frac_of_copy_probe"] = round(res["GBps"] / probes["copy_GBps"], 4)
     res["roofline"]["frac_of_mix_ceiling"] = phases[res["roofline"]["phase"]]["frac_of_mix_ceiling"]
+    # a bf16 expert-major dispatch of the fan-out probe's shape: its rate over
+    # the probe's (the same mix of reads and writes with the simplest addresses)
+    fv, fr, fk = FANOUT_SHAPE
+    if (w is not None and probes.get("fanout_GBps") and "dispatch" in phases
+            and w.quant == 0 and w.mode == 0 and (w.H * 2 // 16, w.N, w.K) == (fv, fr, fk)):
+        phases["dispatch"]["frac_of_fanout_probe"] = round(
+            phases["dispatch"]["GBps"] / probes["fanout_GBps"], 4)
 
 
 def cpu_baseline(w, host, tokens_per_rank, min_seconds):
@@ -699,8 +735,9 @@ def main():
     if not args.no_probes:
         log("[bench] bandwidth probes")
         probes = bandwidth_probes(torch)
-        for r_ in [head[2], *others.values()]:
-            add_mix_ceiling(r_, probes)
+        add_mix_ceiling(head[2], probes, head[0])
+        for name, r_ in others.items():
+            add_mix_ceiling(r_, probes, inputs.WORKLOADS[name])
     w, ms, res = head
     if not args.no_cpu and w.mode != ep.MODE_MESSAGES:
         cpu = cpu_baseline(w, host, min(args.cpu_tokens or w.T, w.T), args.cpu_seconds)

@@ -83,6 +83,34 @@ __global__ __launch_bounds__(256) void probe_copy(const u32x4* __restrict__ src,
   }
 }
 
+// Fan-out: each of `rows` source rows (V vectors) is read once and written to
+// `copies` rows, row k * rows + t (`copies` contiguous destination segments):
+// the bf16 dispatch's read/write mix with the simplest addresses.  One block
+// per source row: 4 waves holding the row in registers (PER = 4 vectors per
+// lane), or 14 waves of one vector each that wait for one copy's stores
+// before the next (PACE).
+template <int PER, bool PACE>
+__global__ __launch_bounds__(1024) void probe_fanout(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int V, int rows,
+                                                     int copies) {
+  const int t = blockIdx.x;
+  u32x4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = threadIdx.x + i * blockDim.x;
+    v[i] = j < V ? src[(int64_t)t * V + j] : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int k = 0; k < copies; ++k) {
+    u32x4* d = dst + ((int64_t)k * rows + t) * V;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = threadIdx.x + i * blockDim.x;
+      if (j < V) d[j] = v[i];
+    }
+    if (PACE) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+}
+
 int64_t chunk_of(int64_t n, int blocks) {
   const int64_t c = (n + blocks - 1) / blocks;
   return (c + 255) / 256 * 256;  // whole rounds of a 256-thread block
@@ -129,4 +157,29 @@ extern "C" int bench_probe_launch(int kind, const void* src, void* dst, int64_t 
     case 17: return launch<8, true>(kind, src, dst, bytes, blocks, s);
     default: return -1;
   }
+}
+
+// Fan-out probe (probe_fanout): src holds rows x row_vectors 16-byte vectors,
+// dst rows x copies x row_vectors.  form 0: four waves, four vectors per lane
+// (row_vectors <= 1024); form 1: one vector per lane, waves paced per copy
+// (row_vectors a multiple of 64, at most 1024).  Returns 0, or -1 for a bad
+// argument or launch error.
+extern "C" int bench_fanout_launch(const void* src, void* dst, int64_t row_vectors, int64_t rows,
+                                   int copies, int form, void* stream) {
+  if (!src || !dst || row_vectors < 1 || row_vectors > 1024 || rows < 1 || rows > (1 << 30) ||
+      copies < 1 || copies > 64)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const int V = (int)row_vectors, n = (int)rows;
+  if (form == 0) {
+    hipLaunchKernelGGL((probe_fanout<4, false>), dim3(n), dim3(256), 0, s, (const u32x4*)src,
+                       (u32x4*)dst, V, n, copies);
+  } else if (form == 1) {
+    if (V % 64 != 0) return -1;
+    hipLaunchKernelGGL((probe_fanout<1, true>), dim3(n), dim3(V), 0, s, (const u32x4*)src,
+                       (u32x4*)dst, V, n, copies);
+  } else {
+    return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -106,3 +106,31 @@ def test_mix_ceiling_adds_read_and_write_times_at_the_probe_rates():
     assert res["mix_ceiling"]["frac"] == 0.5
     assert res["roofline"]["frac_of_mix_ceiling"] == 0.75
     assert res["mix_ceiling"]["frac_of_copy_probe"] == 0.55
+
+
+def test_fanout_fraction_only_for_the_probe_shape():
+    """The dispatch phase of a bf16 expert-major workload with the fan-out
+    probe's shape (rows of 2H bytes, R*T rows, K copies) gets its rate over
+    the probe's; other workloads do not."""
+    from combine_ep_get_layout_amd import inputs
+
+    probes = {"read_GBps": 7000.0, "write_GBps": 6000.0, "copy_GBps": 5500.0,
+              "fanout_GBps": 5000.0}
+
+    def res():
+        return {"phases": {"dispatch": {"ms_mean": 1.0, "read_bytes": 1e9, "written_bytes": 8e9,
+                                        "GBps": 4500.0},
+                           "combine": {"ms_mean": 1.0, "read_bytes": 8e9, "written_bytes": 1e9,
+                                       "GBps": 5000.0}},
+                "bytes_per_step": 18e9, "ms_per_step": 2.0, "GBps": 9000.0,
+                "roofline": {"phase": "dispatch"}}
+
+    w = inputs.WORKLOADS["normal_prefill"]
+    assert (w.H * 2 // 16, w.N, w.K) == bench.FANOUT_SHAPE
+    r = res()
+    bench.add_mix_ceiling(r, probes, w)
+    assert r["phases"]["dispatch"]["frac_of_fanout_probe"] == 0.9
+    for name in ("rank_prefill", "fp8_train", "ll_decode"):
+        r = res()
+        bench.add_mix_ceiling(r, probes, inputs.WORKLOADS[name])
+        assert "frac_of_fanout_probe" not in r["phases"]["dispatch"], name
