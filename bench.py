@@ -540,7 +540,7 @@ def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
         out[name + "_GBps"] = round(best[0], 1)
         out[name + "_config"] = best[1]
     # the bf16 dispatch's mix at the prefill shape: 32,768 rows of 14,336
-    # bytes, each read once and written to 8 rows
+    # bytes, each read once and written to 8 rows (and the combine's below)
     lib.bench_fanout_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p]
@@ -565,10 +565,32 @@ def bandwidth_probes(torch, nbytes=4 << 30, reps=5):
             best = (rate, {"row_bytes": fv * 16, "rows": fr, "copies": fk, "form": form})
     out["fanout_GBps"] = round(best[0], 1)
     out["fanout_config"] = best[1]
+    # and the combine's: each of the 32,768 rows the xor of 8 rows
+    lib.bench_fanin_launch.argtypes = lib.bench_fanout_launch.argtypes
+    lib.bench_fanin_launch.restype = ctypes.c_int
+    best = (0.0, None)
+    for form in (0, 1):
+        def launch():
+            if lib.bench_fanin_launch(a.data_ptr(), b.data_ptr(), fv, fr, fk, form, stream) != 0:
+                raise RuntimeError("fan-in probe launch failed")
+
+        launch()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            launch()
+        e.record()
+        torch.cuda.synchronize()
+        rate = fr * fv * 16 * (1 + fk) / (s.elapsed_time(e) / reps * 1e-3) / 1e9
+        if rate > best[0]:
+            best = (rate, {"row_bytes": fv * 16, "rows": fr, "copies": fk, "form": form})
+    out["fanin_GBps"] = round(best[0], 1)
+    out["fanin_config"] = best[1]
     del a, b, sink
     torch.cuda.empty_cache()
     out["source"] = ("bench_probe.hip (16-byte vector streams, 4 GiB buffers; fan-out: each row "
-                     "read once and written to `copies` contiguous segments)")
+                     "read once and written to `copies` contiguous segments; fan-in: each row "
+                     "the xor of `copies` rows of contiguous segments)")
     return out
 
 
@@ -607,6 +629,10 @@ def add_mix_ceiling(res, probes, w=None):
             and w.quant == 0 and w.mode == 0 and (w.H * 2 // 16, w.N, w.K) == (fv, fr, fk)):
         phases["dispatch"]["frac_of_fanout_probe"] = round(
             phases["dispatch"]["GBps"] / probes["fanout_GBps"], 4)
+        # and its combine over the fan-in probe's
+        if probes.get("fanin_GBps") and "combine" in phases:
+            phases["combine"]["frac_of_fanin_probe"] = round(
+                phases["combine"]["GBps"] / probes["fanin_GBps"], 4)
 
 
 def cpu_baseline(w, host, tokens_per_rank, min_seconds):

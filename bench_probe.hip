@@ -111,6 +111,33 @@ __global__ __launch_bounds__(1024) void probe_fanout(const u32x4* __restrict__ s
   }
 }
 
+// Fan-in: each of `rows` destination rows is the xor of `copies` source rows,
+// row k * rows + t: the bf16 combine's read/write mix with the simplest
+// addresses.  One block per destination row, PER vectors per lane;
+// non-temporal loads and stores, as in the combine.
+template <int PER>
+__global__ __launch_bounds__(1024) void probe_fanin(const u32x4* __restrict__ src,
+                                                    u32x4* __restrict__ dst, int V, int rows,
+                                                    int copies) {
+  const int t = blockIdx.x;
+  u32x4 acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int k = 0; k < copies; ++k) {
+    const u32x4* s = src + ((int64_t)k * rows + t) * V;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = threadIdx.x + i * blockDim.x;
+      if (j < V) acc[i] ^= __builtin_nontemporal_load(s + j);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = threadIdx.x + i * blockDim.x;
+    if (j < V) __builtin_nontemporal_store(acc[i], dst + (int64_t)t * V + j);
+  }
+}
+
 int64_t chunk_of(int64_t n, int blocks) {
   const int64_t c = (n + blocks - 1) / blocks;
   return (c + 255) / 256 * 256;  // whole rounds of a 256-thread block
@@ -177,6 +204,31 @@ extern "C" int bench_fanout_launch(const void* src, void* dst, int64_t row_vecto
   } else if (form == 1) {
     if (V % 64 != 0) return -1;
     hipLaunchKernelGGL((probe_fanout<1, true>), dim3(n), dim3(V), 0, s, (const u32x4*)src,
+                       (u32x4*)dst, V, n, copies);
+  } else {
+    return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Fan-in probe (probe_fanin): src holds copies x rows x row_vectors 16-byte
+// vectors, dst rows x row_vectors.  form 0: one vector per lane (row_vectors
+// a multiple of 64, at most 1024); form 1: four waves, four vectors per lane
+// (row_vectors <= 1024).  Returns 0, or -1 for a bad argument or launch
+// error.
+extern "C" int bench_fanin_launch(const void* src, void* dst, int64_t row_vectors, int64_t rows,
+                                  int copies, int form, void* stream) {
+  if (!src || !dst || row_vectors < 1 || row_vectors > 1024 || rows < 1 || rows > (1 << 30) ||
+      copies < 1 || copies > 64)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const int V = (int)row_vectors, n = (int)rows;
+  if (form == 0) {
+    if (V % 64 != 0) return -1;
+    hipLaunchKernelGGL((probe_fanin<1>), dim3(n), dim3(V), 0, s, (const u32x4*)src,
+                       (u32x4*)dst, V, n, copies);
+  } else if (form == 1) {
+    hipLaunchKernelGGL((probe_fanin<4>), dim3(n), dim3(256), 0, s, (const u32x4*)src,
                        (u32x4*)dst, V, n, copies);
   } else {
     return -1;

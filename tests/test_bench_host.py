@@ -109,13 +109,13 @@ def test_mix_ceiling_adds_read_and_write_times_at_the_probe_rates():
 
 
 def test_fanout_fraction_only_for_the_probe_shape():
-    """The dispatch phase of a bf16 expert-major workload with the fan-out
-    probe's shape (rows of 2H bytes, R*T rows, K copies) gets its rate over
-    the probe's; other workloads do not."""
+    """The dispatch and combine phases of a bf16 expert-major workload with
+    the fan-out / fan-in probes' shape (rows of 2H bytes, R*T rows, K copies)
+    get their rates over the probes'; other workloads do not."""
     from combine_ep_get_layout_amd import inputs
 
     probes = {"read_GBps": 7000.0, "write_GBps": 6000.0, "copy_GBps": 5500.0,
-              "fanout_GBps": 5000.0}
+              "fanout_GBps": 5000.0, "fanin_GBps": 6250.0}
 
     def res():
         return {"phases": {"dispatch": {"ms_mean": 1.0, "read_bytes": 1e9, "written_bytes": 8e9,
@@ -130,7 +130,9 @@ def test_fanout_fraction_only_for_the_probe_shape():
     r = res()
     bench.add_mix_ceiling(r, probes, w)
     assert r["phases"]["dispatch"]["frac_of_fanout_probe"] == 0.9
+    assert r["phases"]["combine"]["frac_of_fanin_probe"] == 0.8
     for name in ("rank_prefill", "fp8_train", "ll_decode"):
         r = res()
         bench.add_mix_ceiling(r, probes, inputs.WORKLOADS[name])
         assert "frac_of_fanout_probe" not in r["phases"]["dispatch"], name
+        assert "frac_of_fanin_probe" not in r["phases"]["combine"], name
