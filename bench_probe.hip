@@ -107,7 +107,8 @@ __global__ __launch_bounds__(1024) void probe_fanout(const u32x4* __restrict__ s
       const int j = threadIdx.x + i * blockDim.x;
       if (j < V) d[j] = v[i];
     }
-    if (PACE) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // s_waitcnt immediate (gfx9 family): vmcnt(0) only (expcnt 7, lgkmcnt 15)
+    if (PACE) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 }
 

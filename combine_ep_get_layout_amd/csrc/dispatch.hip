@@ -263,7 +263,9 @@ __global__ __launch_bounds__(128) void dispatch_copy_lds(const u32x4* __restrict
     // dispatch 766.6 -> 763.6 us over six interleaved runs; waiting after
     // every fourth store or every store took 792 and 804 us, and rank-major
     // rows, about five per token, were 1.3% slower with the per-row wait)
-    if (!RM) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // s_waitcnt immediate (gfx9 family): vmcnt [3:0] and [15:14] = 0,
+    // expcnt [6:4] = 7 and lgkmcnt [11:8] = 15, i.e. only vmcnt(0)
+    if (!RM) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 }
 
