@@ -136,3 +136,30 @@ def test_fanout_fraction_only_for_the_probe_shape():
         bench.add_mix_ceiling(r, probes, inputs.WORKLOADS[name])
         assert "frac_of_fanout_probe" not in r["phases"]["dispatch"], name
         assert "frac_of_fanin_probe" not in r["phases"]["combine"], name
+
+
+def test_probe_library_rejects_bad_arguments_before_any_launch():
+    """The probe entry points check their arguments on the host and return
+    -1 before touching the GPU (so these calls run without one)."""
+    import ctypes
+
+    if not os.path.exists(bench.PROBE_LIB):
+        pytest.skip("libbench_probe.so not built")
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.bench_probe_launch.argtypes = [ctypes.c_int, vp, vp, i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, vp]
+    for f in (lib.bench_fanout_launch, lib.bench_fanin_launch):
+        f.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks
+    assert lib.bench_probe_launch(3, p, p, 1 << 20, 1, 0, 64, None) == -1   # kind
+    assert lib.bench_probe_launch(2, p, p, 1000, 1, 0, 64, None) == -1      # not 16-byte
+    assert lib.bench_probe_launch(2, None, p, 1 << 20, 1, 0, 64, None) == -1
+    assert lib.bench_probe_launch(1, None, p, 1 << 20, 3, 0, 64, None) == -1  # unroll
+    for f in (lib.bench_fanout_launch, lib.bench_fanin_launch):
+        assert f(p, p, 2048, 16, 8, 0, None) == -1    # rows wider than 1024 vectors
+        assert f(p, p, 896, 0, 8, 0, None) == -1      # no rows
+        assert f(p, p, 896, 16, 65, 0, None) == -1    # too many copies
+        assert f(None, p, 896, 16, 8, 0, None) == -1
+        assert f(p, p, 100, 16, 8, 1 if f is lib.bench_fanout_launch else 0, None) == -1
+        assert f(p, p, 896, 16, 8, 2, None) == -1     # form
