@@ -246,18 +246,18 @@ __global__ __launch_bounds__(128) void dispatch_copy_lds(const u32x4* __restrict
   // halves split on a 128-byte line (8 vectors) of the row
   const int half = min(V, ((V + 1) / 2 + 7) & ~7);
   const int lo = wave * half, hi = min(V, lo + half);
-  // expert-major: the token's rows are stored in ascending address order
-  // (lane k < K ranks its row among the token's; measured on MI355X at the
-  // prefill shape: dispatch 763.6 -> 762.0 us over seven interleaved pairs,
-  // every pair faster)
+  // the token's rows are stored in ascending address order (lane k < K
+  // ranks its row among the token's, repeats by k; measured on MI355X at
+  // the prefill routing: expert-major dispatch 763.6 -> 762.0 us over seven
+  // interleaved pairs, rank-major 506.7 -> 503.8 us over four, every pair
+  // faster)
   int rank = 0;
-  if (!RM)
-    for (int k2 = 0; k2 < K; ++k2) {
-      const int r2 = __builtin_amdgcn_readlane(myrow, k2);
-      rank += lane < K && (r2 < myrow || (r2 == myrow && k2 < lane));
-    }
+  for (int k2 = 0; k2 < K; ++k2) {
+    const int r2 = __builtin_amdgcn_readlane(myrow, k2);
+    rank += lane < K && (r2 < myrow || (r2 == myrow && k2 < lane));
+  }
   for (int kk = 0; kk < K; ++kk) {
-    const uint64_t sel = RM ? 0ull : __ballot(lane < K && rank == kk);
+    const uint64_t sel = __ballot(lane < K && rank == kk);
     const int k = sel ? __builtin_ctzll(sel) : kk;
     if (RM && !((keep >> k) & 1)) continue;
     const int row = __builtin_amdgcn_readlane(myrow, k);
