@@ -467,6 +467,8 @@ __global__ __launch_bounds__(256) void scales_to_columns(const uint8_t* __restri
 // shrinks K-fold and is written by consecutive tokens into whole lines.
 // (Measured on MI355X at the FP8 training shape: 27 us; without LDS, four
 // rows per thread gathered word by word and transposed in registers, 38 us.)
+constexpr int kGatherLoads = 8;  // staged-scale words in flight per thread
+
 template <int SB>
 __global__ __launch_bounds__(256) void scales_from_tokens(const uint8_t* __restrict__ stage,
                                                           uint8_t* __restrict__ scales, int G,
@@ -481,18 +483,60 @@ __global__ __launch_bounds__(256) void scales_from_tokens(const uint8_t* __restr
   const int64_t r0 = (int64_t)blockIdx.x * tile_rows;
   if (r0 >= total) return;
   const int nrows = (int)min((int64_t)tile_rows, total - r0);
-  for (int r = threadIdx.x; r < tile_rows; r += blockDim.x) {
-    const int t = r < nrows ? row_token[r0 + r] : -1;
-    tok[r] = t < n_tok ? t : -1;
+  // Every load below is unconditional (indices clamped into the buffers,
+  // values selected afterwards) and a thread issues kGatherLoads of them
+  // before it stores any into LDS: a load under a branch, or a load whose
+  // value is stored before the next is issued, waits for the one before.
+  // (Measured on MI355X at the FP8 training shape, three interleaved runs
+  // each: layout + dispatch 1.0438 -> 1.0390 ms against one gather load per
+  // round trip, which compiled to a wait after every word.)
+  for (int r = threadIdx.x; r < tile_rows; r += 2 * blockDim.x) {
+    const int r2 = r + blockDim.x;
+    const int t1 = row_token[r0 + min(r, nrows - 1)];
+    const int t2 = row_token[r0 + min(r2, nrows - 1)];
+    const int v1 = r < nrows && t1 < n_tok ? t1 : -1;
+    const int v2 = r2 < nrows && t2 < n_tok ? t2 : -1;
+    tok[r] = v1;
+    // unconditional, so the second load is not sunk behind the first
+    // store: past the tile the thread rewrites its own first entry
+    tok[r2 < tile_rows ? r2 : r] = r2 < tile_rows ? v2 : v1;
   }
   __syncthreads();
   const int rb = G * SB;  // bytes of one token's scales
   if (rb % 4 == 0) {
     const int nw = rb / 4;
-    for (int i = threadIdx.x; i < nrows * nw; i += blockDim.x) {
-      const int r = i / nw, q = i - r * nw;
-      const int t = tok[r];
-      ((uint32_t*)tile)[i] = t >= 0 ? ((const uint32_t*)stage)[(int64_t)t * nw + q] : 0u;
+    const int n = nrows * nw;
+    // entry i = (row r, word w) of the tile; one block-wide step of
+    // blockDim.x entries advances (r, w) by (dr, dw)
+    const int bd = blockDim.x;
+    const int dr = bd / nw, dw = bd - dr * nw;
+    int r = threadIdx.x / nw, w = threadIdx.x - r * nw;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kGatherLoads * bd) {
+      int t[kGatherLoads], wq[kGatherLoads];
+#pragma unroll
+      for (int q = 0; q < kGatherLoads; ++q) {
+        const int tv = tok[min(r, tile_rows - 1)];
+        t[q] = i0 + q * bd < n ? tv : -1;
+        wq[q] = w;
+        w += dw;
+        r += dr;
+        const bool wrap = w >= nw;
+        w = wrap ? w - nw : w;
+        r = wrap ? r + 1 : r;
+      }
+      uint32_t v[kGatherLoads];
+#pragma unroll
+      for (int q = 0; q < kGatherLoads; ++q)
+        v[q] = ((const uint32_t*)stage)[(int64_t)(t[q] >= 0 ? t[q] : 0) * nw + wq[q]];
+      // stores are unconditional too (entries past the tile rewrite the
+      // thread's first entry with its own value), so no load is sunk
+      // behind a store
+      const uint32_t first = t[0] >= 0 ? v[0] : 0u;
+#pragma unroll
+      for (int q = 0; q < kGatherLoads; ++q) {
+        const int i = i0 + q * bd;
+        ((uint32_t*)tile)[i < n ? i : i0] = i < n ? (t[q] >= 0 ? v[q] : 0u) : first;
+      }
     }
   } else {
     for (int i = threadIdx.x; i < nrows * rb; i += blockDim.x) {
@@ -508,9 +552,12 @@ __global__ __launch_bounds__(256) void scales_from_tokens(const uint8_t* __restr
   // LDS reads fall in the same few words
   for (int it = threadIdx.x; it < G * nvec; it += blockDim.x) {
     const int g = it % G, rv = (it / G) * kPer;
-    bool full = vec_ok && rv + kPer <= nrows;
+    // rows past the filled ones hold tok = -1 too; one OR over the
+    // vector's rows, with no branch between the LDS reads
+    int neg = 0;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) full = full && tok[rv + q] >= 0;
+    for (int q = 0; q < kPer; ++q) neg |= tok[rv + q];
+    const bool full = vec_ok && rv + kPer <= nrows && neg >= 0;
     const int64_t di = (int64_t)g * cap + r0 + rv;
     if (full) {
       u32x4 v;
@@ -616,7 +663,9 @@ static void launch_fp8_np(const DispatchArgs& a, int P, int waves, hipStream_t s
     if (tok_stage) {
       // the gather from the token staging takes 512-row tiles (measured on
       // MI355X at the training shape: 24 us against 27 us for 256 rows,
-      // 28 us for 128 and 33 us for 1024)
+      // 28 us for 128 and 33 us for 1024, with one gather load per round
+      // trip; with eight in flight, 256-row tiles or sixteen loads per
+      // thread are 1-2 us slower over layout + dispatch)
       tile_rows = 512;
       while (tile_rows > 16 && (size_t)tile_rows * a.g.G * sb > 32768) tile_rows >>= 1;
       const size_t lds = sizeof(int) * (size_t)tile_rows + (size_t)tile_rows * a.g.G * sb;
