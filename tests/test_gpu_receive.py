@@ -33,6 +33,12 @@ CASES = [
     # a 1,240,832-byte arena in 38,776 regions of 32 bytes: region indices
     # near the 16-bit key limit, one descriptor per 32 bytes
     ("r1_1mib_arena_32b_regions", 1, 600, 1024, 2, 2, ep.QUANT_NONE, 32, 0.0, 0.0),
+    # messages of up to 2,400 entries: the receiver ranks and copies them
+    # in two segments of at most 2,048
+    ("r2_two_segments", 2, 300, 256, 8, 8, ep.QUANT_FP8_UE8M0, 4096, 0.1, 0.0),
+    # 128 scale groups per token: more than one per lane of a wavefront
+    ("r2_h16384_f32", 2, 6, 16384, 4, 2, ep.QUANT_FP8_F32, 2 << 20, 0.0, 0.0),
+    ("r2_h16384_ue8m0", 2, 6, 16384, 4, 2, ep.QUANT_FP8_UE8M0, 2 << 20, 0.0, 0.5),
 ]
 FILL = 0x5C
 
