@@ -133,13 +133,57 @@ __global__ __launch_bounds__(256) void layout_count(LayoutArgs a) {
 
 // Exclusive scan, in place, of a row of n = nseg * seg ints; seg_start[j]
 // (LDS) receives the prefix at the start of segment j and seg_start[nseg]
-// the total.  With `relative`, each element is then made relative to its
-// segment's start.
-__device__ void scan_row_segments(int32_t* row, int nseg, int seg, int* seg_start, bool relative) {
+// the total.  With `relative`, each element is made relative to its
+// segment's start.  A thread's PER elements (PER >= per, its share) are
+// loaded together into registers and each final value is stored once: a
+// loop that adds each loaded element before loading the next waits for one
+// memory round trip per element.  (Measured on MI355X, three interleaved
+// runs each: prefill layout 23.5 -> 22.9 us, 64-rank message layout 27.1 ->
+// 26.3 us; with it, 2048 or 4096 target chunks are still slower than 1024.)
+template <int PER>
+__device__ __forceinline__ void scan_row_reg(int32_t* row, int n, int nseg, int seg, int per, int* seg_start,
+                             bool relative) {
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  int v[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int x = row[min(lo + q, n - 1)];  // unconditional, in bounds (n >= 1)
+    v[q] = lo + q < hi ? x : 0;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) sum += v[q];
+  int total;
+  int run = block_exclusive_scan(sum, &total);
+  int pre[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = lo + q;
+    pre[q] = run;
+    if (i < hi && i % seg == 0) seg_start[i / seg] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == 0) seg_start[nseg] = total;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = lo + q;
+    if (i < hi) row[i] = relative ? pre[q] - seg_start[i / seg] : pre[q];
+  }
+}
+
+__device__ __forceinline__ void scan_row_segments(int32_t* row, int nseg, int seg, int* seg_start,
+                                                  bool relative) {
   const int n = nseg * seg;
   for (int j = threadIdx.x; j <= nseg; j += blockDim.x) seg_start[j] = 0;  // empty rows
   __syncthreads();
+  if (n == 0) return;
   const int per = (n + blockDim.x - 1) / blockDim.x;
+  if (per <= 1) return scan_row_reg<1>(row, n, nseg, seg, per, seg_start, relative);
+  if (per <= 2) return scan_row_reg<2>(row, n, nseg, seg, per, seg_start, relative);
+  if (per <= 4) return scan_row_reg<4>(row, n, nseg, seg, per, seg_start, relative);
+  if (per <= 8) return scan_row_reg<8>(row, n, nseg, seg, per, seg_start, relative);
+  // longer rows: element by element
   const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += row[i];
