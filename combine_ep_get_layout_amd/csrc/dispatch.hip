@@ -622,10 +622,19 @@ static void launch_copy_nv(const DispatchArgs& a, int V, int waves, hipStream_t 
 // LDS-staged bf16 copy up to hidden 16384 (32 KiB of LDS per block)
 constexpr int kCopyLdsMaxVectors = 2048;
 
+constexpr size_t kRankMajorLds = 20480;
+
 template <bool RM>
 static void launch_copy_lds(const DispatchArgs& a, int V, hipStream_t st) {
   const int N = a.g.R * a.g.T;
-  const size_t lds = sizeof(u32x4) * (size_t)V;
+  // the row's LDS, which sets how many blocks share a compute unit (160 KiB
+  // of LDS: 11 at hidden 7168).  Rank-major blocks ask for at least 20 KiB,
+  // at most eight per compute unit (measured on MI355X at the prefill
+  // routing, three interleaved runs each: rank-major dispatch 0.5055 ->
+  // 0.5004 ms; the expert-major copy is 0.8% slower with ten blocks, 1.5%
+  // with eight and 5.7% with six, so it keeps the row's size)
+  size_t lds = sizeof(u32x4) * (size_t)V;
+  if (RM && lds < kRankMajorLds) lds = kRankMajorLds;
   if (a.fused)
     hipLaunchKernelGGL((dispatch_copy_lds<false, true>), dim3(fused_blocks(a, N)), dim3(128), lds,
                        st, (const u32x4*)a.x, a.send_pos, (u32x4*)a.recv_x, V, a.g.K, a.cap, a.err,
