@@ -80,6 +80,26 @@ def small_case(c, seed=7):
     return w, align, topk
 
 
+# Chunk counts that give the layout scan three and six chunks per thread
+# (register-held rows, part of the registers unused) and ten (the
+# element-by-element loop), with 1,504, 3,008 and 5,008 chunks; layout only.
+LONG_SCAN = [
+    ("scan_rows_3", 8, 12000, 128, 64, 8, 4, N, QN, 0.05, 0.05, 0),
+    ("scan_rows_6", 16, 12000, 128, 64, 8, 1, N, QN, 0.0, 0.1, 0),
+    ("scan_rows_10", 16, 20000, 128, 64, 8, 2, N, QN, 0.05, 0.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", LONG_SCAN, ids=[c[0] for c in LONG_SCAN])
+def test_layout_long_scan_rows(case):
+    w, align, topk = small_case(case)
+    say("layout", case)
+    p, po = problems(w, align)
+    gl, _ = gpu_layout(p, topk)
+    ol = orc.layout(po, topk)
+    assert_layout_equal(gl, ol, w.mode)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=IDS)
 def test_layout_small(case):
     w, align, topk = small_case(case)
