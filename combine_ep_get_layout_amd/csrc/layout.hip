@@ -44,7 +44,9 @@ __device__ void count_chunk(const LayoutArgs& a, int s, int t_begin, int t_end, 
   const Geometry& g = a.g;
   const int lane = lane_id();
   for (int i = lane; i < g.E + g.R; i += kWave) cnt_e[i] = 0;  // cnt_r follows cnt_e
-  wave_lds_sync();  // zeroed counters before any lane reads them
+  // the row buffer starts cleared; each batch's read-out clears it again
+  for (int i = lane; i < g.tb * g.R; i += kWave) rowbuf[i] = -1;
+  wave_lds_sync();  // zeroed counters and cleared rows before any lane reads them
   const int K = g.K;
   const int my_tok = lane / K, my_k = lane % K;
   const int nent = g.tb * K;
@@ -92,8 +94,6 @@ __device__ void count_chunk(const LayoutArgs& a, int s, int t_begin, int t_end, 
       const uint64_t eqr = match_key((uint32_t)r, g.rbits, vmask);
       const bool first = valid && (eqr & own_below) == 0;
       const uint64_t eqf = eqr & __ballot(first);
-      for (int i = lane; i < g.tb * g.R; i += kWave) rowbuf[i] = -1;
-      wave_lds_sync();  // the cleared row buffer before the first hits land in it
       if (first) {
         const int h = cnt_r[r] + rank_below(eqf);
         rowbuf[my_tok * g.R + r] = h;
@@ -104,11 +104,12 @@ __device__ void count_chunk(const LayoutArgs& a, int s, int t_begin, int t_end, 
       const int64_t rbase = ((int64_t)s * g.T + t0) * g.R;
       for (int i = lane; i < nt * g.R; i += kWave) {
         const int v = rowbuf[i];
+        rowbuf[i] = -1;  // cleared for the next batch (rows past nt stay cleared)
         a.in_rank[rbase + i] = v >= 0 ? 1 : 0;
         a.local_r[rbase + i] = v;
       }
-      // counters advanced by one lane and the row buffer read out, before the
-      // next batch reads the counters and clears the buffer
+      // counters advanced by one lane and the row buffer read out and
+      // cleared, before the next batch reads the counters and fills it
       wave_lds_sync();
     }
   }
